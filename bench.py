@@ -1,0 +1,220 @@
+"""Benchmark: one MoE layer's dispatch + combine on one MI355X.
+
+A step is the whole hot path over one batch: moe_dispatch_send (counts, scans,
+positions, quantise + pack), moe_dispatch_recv (expert-major unpack),
+moe_combine_send and moe_combine_recv, for all N logical ranks.  Inputs are
+seeded synthetic tensors already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+
+
+def algorithmic_bytes(N, T, H, E, k):
+    """Bytes each phase must move (inputs read once, outputs written once)."""
+    P = N * T * k
+    rowq = H + 4 * (H // 128)          # fp8 payload + fp32 scales
+    rowb = 2 * H                       # bf16 row
+    return {
+        "dispatch_send": N * T * 2 * H + P * rowq + 2 * N * T * k * 4 + N * E * 4,
+        "dispatch_recv": 2 * P * rowq,
+        "combine_send": 2 * P * rowb,
+        "combine_recv": P * rowb + N * T * H * 2 + 2 * N * T * k * 4,
+    }
+
+
+def _kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_lds_atomic_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("sources_digest") != _kernel_sources_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(T_sample: int):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    same N, H, E, k with T_sample tokens per rank; single-threaded NumPy."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from oracle import moe_oracle as O
+
+    cfg = W.CONFIGS["combine_heavy"]
+    idx, w = W.routing(cfg, T_sample)
+    x = W.tokens(cfg, "cpu", T_sample).float().numpy()
+    t0 = time.perf_counter()
+    lay = O.layout(idx, cfg.E, cfg.N)
+    rq, rs = O.dispatch_send(x, lay)
+    xq, xs, rsrc = O.dispatch_recv(rq, rs, lay)
+    t1 = time.perf_counter()
+    y = W.expert_outputs(cfg, lay.total_rows, "cpu").view(torch.int16).numpy().view(np.uint16)
+    t2 = time.perf_counter()
+    comb = O.combine_send(y, rsrc, cfg.N, T_sample, cfg.k)
+    O.combine_recv(comb, lay.send_pos, w, T_sample, cfg.k)
+    t3 = time.perf_counter()
+    sec = (t1 - t0) + (t3 - t2)
+    nbytes = sum(algorithmic_bytes(cfg.N, T_sample, cfg.H, cfg.E, cfg.k).values())
+    return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(sec, 2),
+            "sample": f"combine_heavy shape with T={T_sample} tokens/rank (N={cfg.N}, H={cfg.H}, E={cfg.E}, "
+                      f"k={cfg.k}): all four phases, single-threaded NumPy, input generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="combine_heavy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: all N logical EP ranks live in one MI355X's HBM, so --gpus {args.gpus} "
+              "is not a configuration of this benchmark (the multi-GPU sharding is a design, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_lds_atomic_amd as moe
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    T = cfg.Tc if cfg.T_comb else cfg.T
+    if cfg.T_comb and cfg.T_comb != cfg.T:
+        raise SystemExit("bench.py times workloads whose dispatch and combine batches match")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k)
+    idx, w = W.routing(cfg, T)
+    idx_d = torch.from_numpy(idx).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
+    x = W.tokens(cfg, dev, T)
+    B = moe.allocate(sh, dev)
+    y = W.expert_outputs(cfg, B.rows, dev)
+    stream = torch.cuda.current_stream()
+
+    phases = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_dispatch_send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
+        if ev: ev[1].record(stream)
+        moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
+        if ev: ev[2].record(stream)
+        moe.moe_combine_send(sh, y, B.row_src, B.ws, B.comb)
+        if ev: ev[3].record(stream)
+        moe.moe_combine_recv(sh, B.comb, B.send_pos, w_d, B.out)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flags = moe.moe_status(B.ws)
+    if flags:
+        raise SystemExit(f"device error flags {flags:#x} during warm-up")
+
+    # Timed region: exactly K steps, synchronised on both sides.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([[evs[i][p].elapsed_time(evs[i][p + 1]) for p in range(4)] for i in range(args.steps)])
+    per_phase_ms = ms.mean(axis=0)
+    p90_ms = np.percentile(ms, 90, axis=0)
+    step_ms = wall * 1e3 / args.steps
+    nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k)
+    total = sum(nbytes.values())
+
+    # Achievable read+write rate: a plain copy of the dominant phase's bytes.
+    dom = max(range(4), key=lambda p: per_phase_ms[p])
+    copy_bytes = (nbytes[phases[dom]] // 2) // 16 * 16
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        moe.moe_copy(dst, src, copy_bytes)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        moe.moe_copy(dst, src, copy_bytes)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    flags = moe.moe_status(B.ws)
+    if flags:
+        raise SystemExit(f"device error flags {flags:#x} in the timed steps")
+
+    phase_info = {}
+    for p, name in enumerate(phases):
+        gbs = nbytes[name] / (per_phase_ms[p] * 1e-3) / 1e9
+        phase_info[name] = {"us": round(per_phase_ms[p] * 1e3, 1), "p90_us": round(p90_ms[p] * 1e3, 1),
+                            "alg_bytes": nbytes[name], "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom_name = phases[dom]
+    achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
+    kernel = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
+              "combine_recv": "k_comb_recv"}[dom_name]
+    value = total / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": "dispatch / combine us per layer and effective HBM GB/s (% of ~8 TB/s peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}; packed receive regions", "N": cfg.N, "T": T, "H": cfg.H,
+                   "E": cfg.E, "k": cfg.k, "region_rows": 0, "payload": "bf16 in, e4m3fn+fp32 block-128 scales "
+                   "dispatched, bf16 combined with fp32 accumulation"},
+        "phases": phase_info,
+        "dispatch_us": round((per_phase_ms[0] + per_phase_ms[1]) * 1e3, 1),
+        "combine_us": round((per_phase_ms[2] + per_phase_ms[3]) * 1e3, 1),
+        "copy_ceiling_GB/s": round(copy_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(kernel, cfg.name)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

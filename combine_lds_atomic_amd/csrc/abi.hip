@@ -1,0 +1,251 @@
+// Host side of the C ABI declared in include/moe_ep.h: argument checks,
+// workspace carving, grid sizing and launches on the caller's stream.
+#include <mutex>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_u32, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, p, v, n);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by every entry point; fills the derived sizes.
+int make_dims(const moe_shape* sh, Dims* D) {
+  if (!sh) return MOE_ENULL;
+  const moe_shape& s = *sh;
+  if (s.reserved != 0) return MOE_EINVAL;
+  if (s.N < 1 || s.N > kMaxN) return MOE_EINVAL;
+  if (s.T < 0) return MOE_EINVAL;
+  if (s.H < kScaleBlock || s.H > kMaxH || s.H % kScaleBlock) return MOE_EINVAL;
+  if (s.E < 1 || s.E > kMaxE || s.E % s.N) return MOE_EINVAL;
+  if (s.k < 1 || s.k > kMaxK || s.k > s.E) return MOE_EINVAL;
+  if (s.region_rows < 0) return MOE_EINVAL;
+  const int64_t tk = (int64_t)s.T * s.k;
+  const int64_t slots = tk * s.N;
+  if (slots > INT32_MAX) return MOE_ERANGE;
+  const int64_t rows = s.region_rows ? (int64_t)s.N * s.region_rows : slots;
+  if (rows > INT32_MAX) return MOE_ERANGE;
+  D->N = s.N;
+  D->T = s.T;
+  D->H = s.H;
+  D->E = s.E;
+  D->k = s.k;
+  D->L = s.E / s.N;
+  D->TK = (int)tk;
+  D->B = (int)((tk + kChunk - 1) / kChunk);
+  D->NB = s.H / kScaleBlock;
+  D->R = (int)s.region_rows;
+  D->rows = (int)rows;
+  D->bound = (int64_t)s.N * s.T * (s.k > D->L ? s.k : D->L);
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Carve the workspace; returns its total size.  ws may be NULL (sizing only).
+size_t carve(const Dims& D, void* ws, Ws* W) {
+  char* b = static_cast<char*>(ws);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + o : nullptr;
+    o += up(bytes);
+    return p;
+  };
+  char* hdr = take(kAlign);
+  W->err = reinterpret_cast<uint32_t*>(hdr);
+  W->ticket = reinterpret_cast<uint32_t*>(hdr ? hdr + 64 : nullptr);
+  W->blk = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * D.B * D.E));
+  W->cnt = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * D.E));
+  W->send_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.E + 1)));
+  W->recv_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.N + 1)));
+  W->recv_total = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N));
+  W->base = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1)));
+  W->vprefix = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1)));
+  W->exp_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.L + 1)));
+  W->src_in_exp = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1) * D.E));
+  return o;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Grid for a grid-stride kernel over `items` work units of `per_block` each.
+int grid_for(int64_t items, int per_block, int blocks_per_cu) {
+  const int64_t need = (items + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)device_cus() * blocks_per_cu;
+  return (int)(need < 1 ? 1 : (need < cap ? need : cap));
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+inline Ws W_of(const Dims& D, void* ws) {
+  Ws W;
+  carve(D, ws, &W);
+  return W;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_recv_rows(const moe_shape* shape) {
+  Dims D;
+  const int rc = make_dims(shape, &D);
+  return rc ? rc : D.rows;
+}
+
+int64_t moe_workspace_bytes(const moe_shape* shape) {
+  Dims D;
+  const int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  Ws W;
+  return (int64_t)carve(D, nullptr, &W);
+}
+
+int moe_workspace_init(const moe_shape* shape, void* ws, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  return launch_fill_u32(static_cast<uint32_t*>(ws), 0u, (int)(kAlign / sizeof(uint32_t)), as_stream(stream));
+}
+
+int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* recv_q,
+                      float* recv_s, int32_t* send_pos, void* ws, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (D.T == 0) return launch_route(D, W_of(D, ws), topk_idx, send_pos, as_stream(stream));   // empty arrays may be NULL
+  if (!topk_idx || !send_pos) return MOE_ENULL;
+  if (tokens && (!recv_q || !recv_s)) return MOE_ENULL;
+  if (!aligned(ws, kAlign) || !aligned(topk_idx, 4) || !aligned(send_pos, 4)) return MOE_EALIGN;
+  if (tokens && (!aligned(tokens, 16) || !aligned(recv_q, 16) || !aligned(recv_s, 4))) return MOE_EALIGN;
+  Ws W;
+  carve(D, ws, &W);
+  hipStream_t st = as_stream(stream);
+  rc = launch_route(D, W, topk_idx, send_pos, st);
+  if (rc) return rc;
+  return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s,
+                     grid_for((int64_t)D.N * D.T, kWavesPerBlock, 8), st);
+}
+
+int moe_dispatch_recv(const moe_shape* shape, const uint8_t* recv_q, const float* recv_s, const void* ws,
+                      uint8_t* x_q, float* x_s, int32_t* exp_off, int32_t* row_src, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws || !exp_off || (!row_src && D.T > 0)) return MOE_ENULL;
+  const bool payload = recv_q || recv_s || x_q || x_s;
+  if (payload && D.T > 0 && (!recv_q || !recv_s || !x_q || !x_s)) return MOE_ENULL;
+  if (!aligned(ws, kAlign) || !aligned(exp_off, 4) || !aligned(row_src, 4)) return MOE_EALIGN;
+  if (payload && (!aligned(recv_q, 16) || !aligned(x_q, 16) || !aligned(recv_s, 4) || !aligned(x_s, 4)))
+    return MOE_EALIGN;
+  Ws W;
+  carve(D, const_cast<void*>(ws), &W);
+  return launch_unpack(D, W, recv_q, recv_s, x_q, x_s, exp_off, row_src,
+                       grid_for((int64_t)D.rows, kWavesPerBlock * 8, 8), as_stream(stream));
+}
+
+int moe_combine_send(const moe_shape* shape, const uint16_t* y_em, const int32_t* row_src, const void* ws,
+                     uint16_t* comb, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (D.T == 0) return MOE_OK;
+  if (!y_em || !row_src || !comb) return MOE_ENULL;
+  if (!aligned(y_em, 16) || !aligned(comb, 16) || !aligned(row_src, 4) || !aligned(ws, kAlign)) return MOE_EALIGN;
+  Ws W;
+  carve(D, const_cast<void*>(ws), &W);
+  return launch_comb_send(D, W, y_em, row_src, comb, grid_for((int64_t)D.N * D.TK, kWavesPerBlock * 8, 8),
+                          as_stream(stream));
+}
+
+int moe_combine_recv(const moe_shape* shape, const uint16_t* comb, const int32_t* send_pos, const float* topk_w,
+                     uint16_t* out, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (D.T == 0) return MOE_OK;
+  if (!comb || !send_pos || !topk_w || !out) return MOE_ENULL;
+  if (!aligned(comb, 16) || !aligned(out, 16) || !aligned(send_pos, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
+  return launch_comb_recv(D, comb, send_pos, topk_w, out, grid_for((int64_t)D.N * D.T, kWavesPerBlock, 8),
+                          as_stream(stream));
+}
+
+int moe_status(void* ws, void* stream, uint32_t* flags) {
+  if (!ws || !flags) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  hipStream_t st = as_stream(stream);
+  uint32_t h = 0;
+  if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_EHIP;
+  int rc = launch_fill_u32(static_cast<uint32_t*>(ws), 0u, 1, st);
+  if (rc) return rc;
+  *flags = h;
+  return MOE_OK;
+}
+
+int moe_layout_export(const moe_shape* shape, const void* ws, int32_t* cnt, int32_t* send_off, int32_t* recv_off,
+                      int32_t* recv_total, int32_t* base, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  Ws W;
+  carve(D, const_cast<void*>(ws), &W);
+  hipStream_t st = as_stream(stream);
+  struct Item {
+    int32_t* dst;
+    const int* src;
+    size_t n;
+  } items[] = {{cnt, W.cnt, (size_t)D.N * D.E},
+               {send_off, W.send_off, (size_t)D.N * (D.E + 1)},
+               {recv_off, W.recv_off, (size_t)D.N * (D.N + 1)},
+               {recv_total, W.recv_total, (size_t)D.N},
+               {base, W.base, (size_t)D.N + 1}};
+  for (const Item& it : items) {
+    if (!it.dst) continue;
+    if (hipMemcpyAsync(it.dst, it.src, it.n * sizeof(int32_t), hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+int moe_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
+  if (!dst || !src) return MOE_ENULL;
+  if (nbytes < 0 || nbytes % 16) return MOE_EINVAL;
+  if (!aligned(dst, 16) || !aligned(src, 16)) return MOE_EALIGN;
+  return launch_copy(dst, src, nbytes / 16, grid_for(nbytes / 16, kThreads * 4, 8), as_stream(stream));
+}
+
+}  // extern "C"

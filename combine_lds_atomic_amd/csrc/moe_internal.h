@@ -1,0 +1,145 @@
+// Internal definitions shared by the HIP translation units of libmoe_ep.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ep.h"
+
+namespace moe {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kWavesPerBlock = 4;    // 256-thread workgroups everywhere
+constexpr int kThreads = kWave * kWavesPerBlock;
+constexpr int kMaxN = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kMaxH = 32768;
+constexpr int kScaleBlock = 128;     // elements per fp32 scale
+constexpr int kMaxNB = kMaxH / kScaleBlock;
+// Routing chunk: slots of one rank handled by one workgroup of the count
+// kernel; every wave takes a contiguous quarter, 64 slots per batch.
+constexpr int kChunk = 4096;
+constexpr int kPerWave = kChunk / kWavesPerBlock;
+constexpr int kBatches = kPerWave / kWave;
+
+// Problem sizes derived once on the host.
+struct Dims {
+  int N, T, H, E, k;
+  int L;        // experts per rank
+  int TK;       // slots per rank = T*k
+  int B;        // routing chunks per rank
+  int NB;       // scale blocks per row = H/128
+  int R;        // fixed region rows, 0 = packed
+  int rows;     // rows of every receive / expert-major array
+  int64_t bound;  // N*T*max(k, L)
+};
+
+// Workspace tables, all int32 unless noted.
+struct Ws {
+  uint32_t *err;      // sticky MOE_FLAG_* word
+  uint32_t *ticket;   // arrivals of the per-rank scan blocks
+  int *blk;           // [N][B][E] chunk counts, then chunk base positions
+  int *cnt;           // [N][E]
+  int *send_off;      // [N][E+1]
+  int *recv_off;      // [N(dest)][N(src)+1]
+  int *recv_total;    // [N]
+  int *base;          // [N+1] first physical row of each region
+  int *vprefix;       // [N+1] running total of rows written per region
+  int *exp_off;       // [N][L+1]
+  int *src_in_exp;    // [N+1][E] rows of expert e from sources before s
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// One DPP move inside rows of 16 lanes; all lanes active.
+template <int Ctrl>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, 0xF, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i inside 8 lanes
+
+// Max over each aligned group of 8 lanes, for non-negative float bit
+// patterns compared as integers (exact for finite values).
+__device__ __forceinline__ int max8_lanes(int v) {
+  v = max(v, dpp_mov<kDppQuadXor1>(v));
+  v = max(v, dpp_mov<kDppQuadXor2>(v));
+  v = max(v, dpp_mov<kDppHalfMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// float32 -> OCP E4M3 (e4m3fn) byte, round to nearest even, saturating to
+// +-448; NaN -> S.1111.111.  Bit manipulation on the IEEE pattern.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;        // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;       // >= 448: RNE gives 448 up to 464, saturate above
+  if (a < 0x3C800000u) {                           // below 2^-6: subnormal spacing 2^-9
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
+    return sign | (uint32_t)m;                     // m == 8 is the smallest normal, 0x08
+  }
+  // Normal range: keep 3 of the 23 mantissa bits, ties to even; a carry
+  // moves into the exponent.  Rebias 127 -> 7.
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
+}
+
+// Copy n16 16-byte units from src to dst with the whole wave; each lane
+// issues up to U loads before its stores.
+template <int U>
+__device__ __forceinline__ void wave_copy16(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16, int lane) {
+  for (int c0 = 0; c0 < n16; c0 += kWave * U) {
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      r[u] = c < n16 ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < n16) dst[c] = r[u];
+    }
+  }
+}
+
+// Largest i in [0, n) with a[i*stride] <= v, for non-decreasing a with a[0] <= v.
+__device__ __forceinline__ int floor_index(const int* a, int n, int v, int stride = 1) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a[(int64_t)mid * stride] <= v) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Launchers (one per translation unit that owns the kernels).
+int launch_route(const Dims& D, const Ws& W, const int* idx, int* send_pos, hipStream_t st);
+int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
+                float* recv_s, int grid, hipStream_t st);
+int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
+                  int* exp_off, int* row_src, int grid, hipStream_t st);
+int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int grid,
+                     hipStream_t st);
+int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int grid,
+                     hipStream_t st);
+int launch_copy(void* dst, const void* src, int64_t n16, int grid, hipStream_t st);
+int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
+
+}  // namespace moe

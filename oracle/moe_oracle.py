@@ -276,11 +276,18 @@ def layout(idx, E: int, N: int, region_rows: int = 0) -> Layout:
     l = e - d * L
     in_region = recv_off[d, s_of] + (send_pos - send_off[s_of, d * L])
     in_em = exp_off[d, l] + src_in_exp[s_of, e] + (send_pos - send_off[s_of, e])
-    fits = valid if region_rows == 0 else valid & (in_region < region_rows) & (in_em < region_rows)
-    recv_row = np.where(fits, base[d] + in_region, -1)
-    em_row = np.where(fits, base[d] + in_em, -1)
-    if region_rows and (fits != valid).any():
-        flags |= FLAG_OVERFLOW
+    # A fixed region keeps the rows that fit it: a source-major row exists if
+    # its region row is below R; an expert-major row exists if its own index
+    # and its source-major row are both below R.
+    if region_rows == 0:
+        recv_fits = em_fits = valid
+    else:
+        recv_fits = valid & (in_region < region_rows)
+        em_fits = recv_fits & (in_em < region_rows)
+        if (recv_fits != valid).any():
+            flags |= FLAG_OVERFLOW
+    recv_row = np.where(recv_fits, base[d] + in_region, -1)
+    em_row = np.where(em_fits, base[d] + in_em, -1)
 
     return Layout(N=N, T=T, E=E, k=k, L=L, region_rows=region_rows, cnt=cnt,
                   send_off=send_off, send_pos=send_pos, recv_off=recv_off,

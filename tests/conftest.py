@@ -10,6 +10,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # The library is built in-tree ahead of time; build it here only if nothing is built.
+    if not os.path.exists(os.path.join(ROOT, "combine_lds_atomic_amd", "libmoe_ep.so")):
+        import runpy   # by path: importing the package itself needs the built library
+        runpy.run_path(os.path.join(ROOT, "combine_lds_atomic_amd", "build.py"))["build"]()
 
 
 def pytest_collection_modifyitems(config, items):

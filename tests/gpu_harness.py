@@ -1,0 +1,126 @@
+"""Helpers shared by the GPU tests: run the four C-ABI calls on seeded inputs
+and compare with the oracle.  Nothing here computes expected values itself --
+they come from ``oracle`` only."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import combine_lds_atomic_amd as moe
+import workloads as W
+from oracle import moe_oracle as O
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 tensor -> uint16 bit patterns on the host."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_all(cfg: W.Config, T: int, region_rows: int = 0, idx=None, w=None, x=None, y=None,
+            payload: bool = True, combine: bool = True, fill: int | None = 0x5A, device="cuda"):
+    """Generate (or take) inputs and run dispatch send/recv and combine send/recv."""
+    sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, region_rows)
+    if idx is None:
+        idx, w = W.routing(cfg, T)
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(device)
+    w_d = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(device)
+    if x is None and payload:
+        x = W.tokens(cfg, device, T)
+    B = moe.allocate(sh, device, payload=payload, combine=combine, fill_rows=fill)
+    moe.moe_dispatch_send(sh, x if payload else None, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
+    moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
+    if combine:
+        if y is None:
+            y = W.expert_outputs(cfg, B.rows, device)
+        if fill is not None:
+            B.comb.view(torch.int16).fill_(0x3F00)
+        moe.moe_combine_send(sh, y, B.row_src, B.ws, B.comb)
+        moe.moe_combine_recv(sh, B.comb, B.send_pos, w_d, B.out)
+    flags = moe.moe_status(B.ws)
+    return dict(sh=sh, idx=np.asarray(idx), w=np.asarray(w), x=x, y=y, B=B, flags=flags)
+
+
+def export_layout(r):
+    sh, B = r["sh"], r["B"]
+    N, E = sh.N, sh.E
+    dev = B.ws.device
+    t = dict(cnt=torch.empty((N, E), dtype=torch.int32, device=dev),
+             send_off=torch.empty((N, E + 1), dtype=torch.int32, device=dev),
+             recv_off=torch.empty((N, N + 1), dtype=torch.int32, device=dev),
+             recv_total=torch.empty((N,), dtype=torch.int32, device=dev),
+             base=torch.empty((N + 1,), dtype=torch.int32, device=dev))
+    moe.moe_layout_export(sh, B.ws, **t)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in t.items()}
+
+
+def check_layout(r, lay: O.Layout):
+    """Counts, offsets, positions, exp_off and row_src: bit-exact."""
+    g = export_layout(r)
+    B = r["B"]
+    assert (g["cnt"] == lay.cnt).all(), "cnt"
+    assert (g["send_off"] == lay.send_off).all(), "send_off"
+    assert (g["recv_off"] == lay.recv_off).all(), "recv_off"
+    assert (g["recv_total"] == lay.recv_total).all(), "recv_total"
+    assert (g["base"] == lay.base).all(), "base"
+    assert (B.send_pos.cpu().numpy() == lay.send_pos).all(), "send_pos"
+    assert (B.exp_off.cpu().numpy() == lay.exp_off).all(), "exp_off"
+    rs = B.row_src.cpu().numpy()
+    want = O.row_src(lay)
+    used = O.region_rows_used(lay)
+    for d in range(lay.N):
+        a, b = lay.base[d], lay.base[d] + used[d]
+        assert (rs[a:b] == want[a:b]).all(), f"row_src region {d}"
+
+
+def check_full(r, lay: O.Layout, check_comb=True):
+    """Whole-buffer parity against the oracle (small cases)."""
+    check_layout(r, lay)
+    B = r["B"]
+    sh = r["sh"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    if B.recv_q is not None:
+        x = r["x"].float().cpu().numpy()
+        rq, rs = O.dispatch_send(x, lay)
+        xq, xs, _ = O.dispatch_recv(rq, rs, lay)
+        got_rq, got_rs = B.recv_q.cpu().numpy(), B.recv_s.cpu().numpy()
+        got_xq, got_xs = B.x_q.cpu().numpy(), B.x_s.cpu().numpy()
+        rrow = lay.recv_row[lay.recv_row >= 0]
+        erow = lay.em_row[lay.em_row >= 0]
+        assert (got_rq[rrow] == rq[rrow]).all(), "recv_q"
+        assert (got_rs[rrow].view(np.uint32) == rs[rrow].view(np.uint32)).all(), "recv_s"
+        assert (got_xq[erow] == xq[erow]).all(), "x_q"
+        assert (got_xs[erow].view(np.uint32) == xs[erow].view(np.uint32)).all(), "x_s"
+        # rows nobody writes keep the fill pattern
+        untouched = np.setdiff1d(np.arange(B.rows), rrow)
+        assert (got_rq[untouched] == 0x5A).all(), "recv_q rows outside the regions were written"
+    if check_comb and B.comb is not None:
+        y = bf16_np(r["y"])
+        rsrc = O.row_src(lay)
+        comb = O.combine_send(y, rsrc, N, T, k)
+        got_comb = bf16_np(B.comb).reshape(N * T * k, H)
+        wr = rsrc[rsrc >= 0]
+        assert (got_comb[wr] == comb[wr]).all(), "comb"
+        out = O.combine_recv(comb, lay.send_pos, r["w"], T, k)
+        got_out = bf16_np(B.out)
+        check_combine_out(got_out, out)
+
+
+def check_combine_out(got: np.ndarray, ref: np.ndarray):
+    """bf16 combine output: the stated tolerance (1 bf16 ulp per element and
+    |d| <= 2^-7 |ref| + 1e-3); the kernel also claims bit-exactness (same
+    float32 operations in the same order, no FMA)."""
+    g = O.bf16_from_bits(got).astype(np.float64)
+    f = O.bf16_from_bits(ref).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(f))[1] - 8)
+    d = np.abs(g - f)
+    assert (d <= np.maximum(ulp, 2.0 ** -133)).all(), f"combine off by more than 1 ulp: max {d.max()}"
+    assert (d <= 2.0 ** -7 * np.abs(f) + 1e-3).all(), "combine outside abs/rel tolerance"
+    assert (got == ref).all(), f"combine not bit-exact at {np.count_nonzero(got != ref)} elements"
