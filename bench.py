@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="combine_heavy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: all N logical EP ranks live in one MI355X's HBM, so --gpus {args.gpus} "

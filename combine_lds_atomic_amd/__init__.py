@@ -41,7 +41,27 @@ def shape(N: int, T: int, H: int, E: int, k: int, region_rows: int = 0) -> moe_s
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_lds_atomic_amd.build` "
                       "(or __graft_entry__.build()) first")
+
+# torch ships its own HIP runtime.  It must be in the process before the
+# library is opened, so that the library's libamdhip64.so.7 dependency binds to
+# that same runtime (by soname) instead of loading a second one: with two
+# runtimes the library sees no device and torch's streams mean nothing to it.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes() -> set[str]:
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:  # pragma: no cover
+        return set()
+    return {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded ({sorted(_hip_runtimes())}); import torch before anything "
+                      "that links /opt/rocm's libamdhip64")
 
 _P = ctypes.c_void_p
 _S = ctypes.POINTER(moe_shape)

@@ -21,7 +21,10 @@ SOURCES = ["abi.hip", "layout.hip", "dispatch.hip", "combine.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
+# Code object v5: the HIP runtime that ships with PyTorch (ROCm 7.0) is the one
+# loaded in the process, so the device code must be in a version it accepts.
 HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
+               "-mcode-object-version=5",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -11,8 +11,7 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, int n) {
 }
 
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_u32, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, p, v, n);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_fill_u32", k_fill_u32, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, p, v, n);
 }
 
 namespace {

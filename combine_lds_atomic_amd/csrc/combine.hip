@@ -130,22 +130,19 @@ __global__ __launch_bounds__(kThreads) void k_copy16(uint4* __restrict__ dst, co
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int grid,
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
-  hipLaunchKernelGGL(k_comb_send, dim3(grid), dim3(kThreads), 0, st, D, W, y, row_src, comb);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kThreads), 0, st, D, W, y, row_src, comb);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int grid,
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  hipLaunchKernelGGL(k_comb_recv, dim3(grid), dim3(kThreads), 0, st, D, comb, send_pos, w, out);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_comb_recv", k_comb_recv, dim3(grid), dim3(kThreads), 0, st, D, comb, send_pos, w, out);
 }
 
 int launch_copy(void* dst, const void* src, int64_t n16, int grid, hipStream_t st) {
   if (n16 == 0) return MOE_OK;
-  hipLaunchKernelGGL(k_copy16, dim3(grid), dim3(kThreads), 0, st, reinterpret_cast<uint4*>(dst),
-                     reinterpret_cast<const uint4*>(src), n16);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_copy16", k_copy16, dim3(grid), dim3(kThreads), 0, st, reinterpret_cast<uint4*>(dst),
+                reinterpret_cast<const uint4*>(src), n16);
 }
 
 }  // namespace moe

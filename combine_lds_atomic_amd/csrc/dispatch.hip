@@ -141,14 +141,13 @@ __global__ __launch_bounds__(kThreads) void k_unpack(Dims D, Ws W, const uint8_t
 int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
                 float* recv_s, int grid, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  hipLaunchKernelGGL(k_pack, dim3(grid), dim3(kThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_pack", k_pack, dim3(grid), dim3(kThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_unpack, dim3(grid), dim3(kThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off, row_src);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_unpack", k_unpack, dim3(grid), dim3(kThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
+                row_src);
 }
 
 }  // namespace moe

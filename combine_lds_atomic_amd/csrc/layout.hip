@@ -218,15 +218,14 @@ __global__ __launch_bounds__(kThreads) void k_route_scan(Dims D, Ws W) {
 int launch_route(const Dims& D, const Ws& W, const int* idx, int* send_pos, hipStream_t st) {
   if (D.B > 0) {
     const size_t lds = (size_t)kWavesPerBlock * D.E * (sizeof(unsigned long long) + sizeof(int));
-    hipLaunchKernelGGL(k_route_count, dim3(D.B, D.N), dim3(kThreads), lds, st, D, W, idx, send_pos);
-    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+    const int rc = launch("k_route_count", k_route_count, dim3(D.B, D.N), dim3(kThreads), lds, st, D, W, idx, send_pos);
+    if (rc != MOE_OK) return rc;
   } else {
     // No slots: the scan still publishes zero counts; reset the ticket.
     const int rc = launch_fill_u32(W.ticket, 0u, 1, st);
     if (rc != MOE_OK) return rc;
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(D.N), dim3(kThreads), 0, st, D, W);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  return launch("k_route_scan", k_route_scan, dim3(D.N), dim3(kThreads), 0, st, D, W);
 }
 
 }  // namespace moe

@@ -3,10 +3,34 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <tuple>
+#include <utility>
 
 #include "moe_ep.h"
 
 namespace moe {
+
+// Launch `k` on `st` and return the launch's own status (hipLaunchKernel
+// reports it directly, so an earlier error left by another library in the
+// same thread is neither reported nor cleared).
+template <typename... KArgs, typename... Args>
+int launch(const char* name, void (*k)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+           Args&&... args) {
+  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, lds, st);
+  if (e != hipSuccess) {
+    fprintf(stderr, "libmoe_ep: launching %s failed: %s (%d)\n", name, hipGetErrorString(e), (int)e);
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
 
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerBlock = 4;    // 256-thread workgroups everywhere
