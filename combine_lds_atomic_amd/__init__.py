@@ -11,7 +11,8 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_ep.so")
+# MOE_EP_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_EP_LIB") or os.path.join(PKG, "libmoe_ep.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe_ep.h")
 
 MOE_OK = 0

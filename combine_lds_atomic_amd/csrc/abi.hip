@@ -91,13 +91,6 @@ int device_cus() {
   return cache[dev];
 }
 
-// Grid for a grid-stride kernel over `items` work units of `per_block` each.
-int grid_for(int64_t items, int per_block, int blocks_per_cu) {
-  const int64_t need = (items + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)device_cus() * blocks_per_cu;
-  return (int)(need < 1 ? 1 : (need < cap ? need : cap));
-}
-
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 inline Ws W_of(const Dims& D, void* ws) {
@@ -142,6 +135,7 @@ int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int3
   int rc = make_dims(shape, &D);
   if (rc) return rc;
   if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
   if (D.T == 0) return launch_route(D, W_of(D, ws), topk_idx, send_pos, as_stream(stream));   // empty arrays may be NULL
   if (!topk_idx || !send_pos) return MOE_ENULL;
   if (tokens && (!recv_q || !recv_s)) return MOE_ENULL;
@@ -152,8 +146,7 @@ int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int3
   hipStream_t st = as_stream(stream);
   rc = launch_route(D, W, topk_idx, send_pos, st);
   if (rc) return rc;
-  return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s,
-                     grid_for((int64_t)D.N * D.T, kWavesPerBlock, 8), st);
+  return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s, device_cus(), st);
 }
 
 int moe_dispatch_recv(const moe_shape* shape, const uint8_t* recv_q, const float* recv_s, const void* ws,
@@ -169,8 +162,7 @@ int moe_dispatch_recv(const moe_shape* shape, const uint8_t* recv_q, const float
     return MOE_EALIGN;
   Ws W;
   carve(D, const_cast<void*>(ws), &W);
-  return launch_unpack(D, W, recv_q, recv_s, x_q, x_s, exp_off, row_src,
-                       grid_for((int64_t)D.rows, kWavesPerBlock * 8, 8), as_stream(stream));
+  return launch_unpack(D, W, recv_q, recv_s, x_q, x_s, exp_off, row_src, device_cus(), as_stream(stream));
 }
 
 int moe_combine_send(const moe_shape* shape, const uint16_t* y_em, const int32_t* row_src, const void* ws,
@@ -184,8 +176,7 @@ int moe_combine_send(const moe_shape* shape, const uint16_t* y_em, const int32_t
   if (!aligned(y_em, 16) || !aligned(comb, 16) || !aligned(row_src, 4) || !aligned(ws, kAlign)) return MOE_EALIGN;
   Ws W;
   carve(D, const_cast<void*>(ws), &W);
-  return launch_comb_send(D, W, y_em, row_src, comb, grid_for((int64_t)D.N * D.TK, kWavesPerBlock * 8, 8),
-                          as_stream(stream));
+  return launch_comb_send(D, W, y_em, row_src, comb, device_cus(), as_stream(stream));
 }
 
 int moe_combine_recv(const moe_shape* shape, const uint16_t* comb, const int32_t* send_pos, const float* topk_w,
@@ -196,7 +187,7 @@ int moe_combine_recv(const moe_shape* shape, const uint16_t* comb, const int32_t
   if (D.T == 0) return MOE_OK;
   if (!comb || !send_pos || !topk_w || !out) return MOE_ENULL;
   if (!aligned(comb, 16) || !aligned(out, 16) || !aligned(send_pos, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
-  return launch_comb_recv(D, comb, send_pos, topk_w, out, grid_for((int64_t)D.N * D.T, kWavesPerBlock, 8),
+  return launch_comb_recv(D, comb, send_pos, topk_w, out, device_cus(),
                           as_stream(stream));
 }
 
@@ -244,7 +235,7 @@ int moe_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
   if (!dst || !src) return MOE_ENULL;
   if (nbytes < 0 || nbytes % 16) return MOE_EINVAL;
   if (!aligned(dst, 16) || !aligned(src, 16)) return MOE_EALIGN;
-  return launch_copy(dst, src, nbytes / 16, grid_for(nbytes / 16, kThreads * 4, 8), as_stream(stream));
+  return launch_copy(dst, src, nbytes / 16, device_cus(), as_stream(stream));
 }
 
 }  // extern "C"

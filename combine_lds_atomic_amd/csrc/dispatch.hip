@@ -2,23 +2,65 @@
 // sections "Send and receive buffers", "Dispatch and combine", and
 // "Evaluation: dispatch/combine latency" for the block-scaled fp8 payload).
 //
-//   k_pack    one wave per token: final slot positions, block-128 amax with
-//             DPP, fp8 quantisation, and k 16-byte row stores straight into
-//             the destination ranks' receive regions (the "remote write").
-//   k_unpack  one wave per 8 expert-major rows: the receive side finds each
-//             row's (expert, source) segment from the exchanged counts alone
-//             and copies it out of the source-major receive region.
+//   k_pack    each workgroup streams a contiguous range of tokens, one wave
+//             per token: final slot positions, block-128 amax with DPP, fp8
+//             quantisation, and k 16-byte row stores straight into the
+//             destination ranks' receive regions (the "remote write").
+//   k_unpack  each workgroup streams a contiguous range of expert-major rows:
+//             the receive side finds each row's (expert, source) segment from
+//             the exchanged counts alone and copies it out of the
+//             source-major receive region.
 #include "moe_internal.h"
+
+// fp32 -> e4m3fn conversion.  Both variants give the same bytes on the
+// whole input domain (every bfloat16 pair x <= amax), which the exhaustive
+// sweep test checks against the oracle:
+//   MOE_PACK_CVT 0: round with integer operations on the float's bits;
+//                1: v_cvt_pk_fp8_f32 (on gfx950 it converts to OCP e4m3fn,
+//                   round to nearest even), two values per instruction.
+#ifndef MOE_PACK_CVT
+#define MOE_PACK_CVT 1
+#endif
+#ifndef MOE_PACK_PASSES
+#define MOE_PACK_PASSES 4
+#endif
+// Store order of the k copies: 0 = pass by pass (1 KB to each destination in
+// turn), 1 = the whole row to one destination, then the next.
+#ifndef MOE_PACK_ROW_STORES
+#define MOE_PACK_ROW_STORES 0
+#endif
 
 namespace moe {
 
-__global__ __launch_bounds__(kThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
-                                                   const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                   uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
-  __shared__ float sscale[kWavesPerBlock][kMaxNB];
+constexpr int kPkWaves = kPackShape.waves, kPkThreads = kPackShape.threads();
+constexpr int kUpWaves = kUnpackShape.waves, kUpThreads = kUnpackShape.threads();
+constexpr int kPackCols = kWave * 16;         // elements one wave covers per pass (16 per lane)
+constexpr int kPackPasses = MOE_PACK_PASSES;  // passes whose loads are issued together
+
+// Four quotients x[i] / scale (IEEE division) packed as e4m3fn bytes,
+// little end first.
+__device__ __forceinline__ uint32_t quant4(const float* v, float scale) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = v[i] / scale;
+#if MOE_PACK_CVT
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+  return (uint32_t)w;
+#else
+  return f32_to_e4m3fn(q[0]) | (f32_to_e4m3fn(q[1]) << 8) | (f32_to_e4m3fn(q[2]) << 16) |
+         (f32_to_e4m3fn(q[3]) << 24);
+#endif
+}
+
+__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                     const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
+  __shared__ float sscale[kPkWaves][kMaxNB];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int NT = D.N * D.T;
-  for (int tok = blockIdx.x * kWavesPerBlock + wv; tok < NT; tok += gridDim.x * kWavesPerBlock) {
+  int lo, hi;
+  block_range(D.N * D.T, lo, hi);
+  for (int tok = lo + wv; tok < hi; tok += kPkWaves) {
     const int s = tok / D.T, t = tok - s * D.T;
     // Lane j < k resolves slot j: position = chunk base of its expert + rank
     // inside the chunk (left in send_pos by the count kernel).
@@ -39,41 +81,64 @@ __global__ __launch_bounds__(kThreads) void k_pack(Dims D, Ws W, const uint16_t*
     if (x == nullptr) continue;
 
     const uint16_t* xr = x + (int64_t)tok * D.H;
-    for (int c0 = 0; c0 < D.H; c0 += kWave * 16) {
-      const int col = c0 + lane * 16;          // this lane's 16 elements
-      const bool act = col < D.H;              // whole 8-lane groups drop out together
-      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-      if (act) {
-        a = *reinterpret_cast<const uint4*>(xr + col);
-        b = *reinterpret_cast<const uint4*>(xr + col + 8);
-      }
-      const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      float v[16];
+    for (int c0 = 0; c0 < D.H; c0 += kPackCols * kPackPasses) {
+      // Issue the loads of several passes before any math.
+      v4u a[kPackPasses], b[kPackPasses];
+#if MOE_PACK_ROW_STORES
+      v4u qs[kPackPasses];
+#endif
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = bf16_lo(wds[i]);
-        v[2 * i + 1] = bf16_hi(wds[i]);
+      for (int p = 0; p < kPackPasses; ++p) {
+        const int col = c0 + p * kPackCols + lane * 16;
+        const bool act = col < D.H;
+        a[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col)) : v4u{0, 0, 0, 0};
+        b[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col + 8)) : v4u{0, 0, 0, 0};
       }
-      int am = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
-      am = max8_lanes(am);                     // amax of the 128-element block
-      const float amax = __uint_as_float((uint32_t)am);
-      const float scale = amax / 448.0f;       // IEEE division, round to nearest even
-      uint32_t q[4] = {0, 0, 0, 0};
-      if (amax != 0.0f) {
+      for (int p = 0; p < kPackPasses; ++p) {
+        if (c0 + p * kPackCols >= D.H) break;
+        const int col = c0 + p * kPackCols + lane * 16;   // this lane's 16 elements
+        const bool act = col < D.H;                         // whole 8-lane groups drop out together
+        float v[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          q[i] = f32_to_e4m3fn(v[4 * i] / scale) | (f32_to_e4m3fn(v[4 * i + 1] / scale) << 8) |
-                 (f32_to_e4m3fn(v[4 * i + 2] / scale) << 16) | (f32_to_e4m3fn(v[4 * i + 3] / scale) << 24);
+          v[2 * i] = bf16_lo(a[p][i]);
+          v[2 * i + 1] = bf16_hi(a[p][i]);
+          v[8 + 2 * i] = bf16_lo(b[p][i]);
+          v[8 + 2 * i + 1] = bf16_hi(b[p][i]);
         }
+        int am = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
+        am = max8_lanes(am);                     // amax of the 128-element block
+        const float amax = __uint_as_float((uint32_t)am);
+        const float scale = amax / 448.0f;       // IEEE division, round to nearest even
+        v4u q = {0, 0, 0, 0};
+        if (amax != 0.0f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
+        }
+        if (act && (lane & 7) == 0) sscale[wv][col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
+#if MOE_PACK_ROW_STORES
+        qs[p] = q;
+#else
+        for (int j = 0; j < D.k; ++j) {
+          const int rj = __builtin_amdgcn_readlane(row, j);
+          if (rj >= 0 && act) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), q);
+        }
+#endif
       }
-      if (act && (lane & 7) == 0) sscale[wv][col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
-      const uint4 qv = make_uint4(q[0], q[1], q[2], q[3]);
+#if MOE_PACK_ROW_STORES
       for (int j = 0; j < D.k; ++j) {
         const int rj = __builtin_amdgcn_readlane(row, j);
-        if (rj >= 0 && act) *reinterpret_cast<uint4*>(recv_q + (int64_t)rj * D.H + col) = qv;
+        if (rj < 0) continue;
+#pragma unroll
+        for (int p = 0; p < kPackPasses; ++p) {
+          const int col = c0 + p * kPackCols + lane * 16;
+          if (col < D.H) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), qs[p]);
+        }
       }
+#endif
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -88,25 +153,26 @@ __global__ __launch_bounds__(kThreads) void k_pack(Dims D, Ws W, const uint16_t*
   }
 }
 
-constexpr int kRowsPerWave = 8;
+constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
 
-__global__ __launch_bounds__(kThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
-                                                     const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
-                                                     float* __restrict__ x_s, int* __restrict__ exp_off,
-                                                     int* __restrict__ row_src) {
+__global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
+                                                       const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
+                                                       float* __restrict__ x_s, int* __restrict__ exp_off,
+                                                       int* __restrict__ row_src) {
   __shared__ int svp[kMaxN + 1];
-  for (int i = threadIdx.x; i <= D.N; i += kThreads) svp[i] = W.vprefix[i];
+  for (int i = threadIdx.x; i <= D.N; i += kUpThreads) svp[i] = W.vprefix[i];
   if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kThreads) exp_off[i] = W.exp_off[i];
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kUpThreads) exp_off[i] = W.exp_off[i];
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int total = svp[D.N];
   const int N = D.N, E = D.E, L = D.L;
-  for (int g0 = (blockIdx.x * kWavesPerBlock + wv) * kRowsPerWave; g0 < total;
-       g0 += gridDim.x * kWavesPerBlock * kRowsPerWave) {
+  const bool scales16 = (D.NB & 3) == 0;   // scale rows are whole 16-byte units
+  int lo, hi;
+  block_range(svp[N], lo, hi);        // valid rows, in region order
+  for (int g0 = lo + wv; g0 < hi; g0 += kUpWaves * kRowsPerPass) {
     int src = -1, dst = -1;
-    if (lane < kRowsPerWave && g0 + lane < total) {
-      const int g = g0 + lane;
+    const int g = g0 + lane * kUpWaves;
+    if (lane < kRowsPerPass && g < hi) {
       const int d = floor_index(svp, N + 1, g);
       const int i = g - svp[d];                                  // expert-major row inside region d
       const int* eo = W.exp_off + d * (L + 1);
@@ -127,26 +193,38 @@ __global__ __launch_bounds__(kThreads) void k_unpack(Dims D, Ws W, const uint8_t
       }
     }
     if (x_q == nullptr) continue;   // layout only
-    for (int r = 0; r < kRowsPerWave; ++r) {
+    for (int r = 0; r < kRowsPerPass; ++r) {
       const int sr = __builtin_amdgcn_readlane(src, r);
       const int dr = __builtin_amdgcn_readlane(dst, r);
       if (sr < 0 || dr < 0) continue;
-      wave_copy16<8>(reinterpret_cast<uint4*>(x_q + (int64_t)dr * D.H),
-                     reinterpret_cast<const uint4*>(recv_q + (int64_t)sr * D.H), D.H / 16, lane);
-      for (int c = lane; c < D.NB; c += kWave) x_s[(int64_t)dr * D.NB + c] = recv_s[(int64_t)sr * D.NB + c];
+      wave_copy16<8>(reinterpret_cast<v4u*>(x_q + (int64_t)dr * D.H),
+                     reinterpret_cast<const v4u*>(recv_q + (int64_t)sr * D.H), D.H / 16, lane);
+      if (scales16) {
+        const int n16 = D.NB / 4;
+        if (lane < n16)
+          st16(reinterpret_cast<v4u*>(x_s + (int64_t)dr * D.NB) + lane,
+               ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)sr * D.NB) + lane));
+        for (int c = lane + kWave; c < n16; c += kWave)
+          st16(reinterpret_cast<v4u*>(x_s + (int64_t)dr * D.NB) + c,
+               ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)sr * D.NB) + c));
+      } else {
+        for (int c = lane; c < D.NB; c += kWave) x_s[(int64_t)dr * D.NB + c] = recv_s[(int64_t)sr * D.NB + c];
+      }
     }
   }
 }
 
 int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
-                float* recv_s, int grid, hipStream_t st) {
+                float* recv_s, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  return launch("k_pack", k_pack, dim3(grid), dim3(kThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
+  const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T, kPkWaves);
+  return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
-                  int* exp_off, int* row_src, int grid, hipStream_t st) {
-  return launch("k_unpack", k_unpack, dim3(grid), dim3(kThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
+                  int* exp_off, int* row_src, int cus, hipStream_t st) {
+  const int grid = stream_grid(kUnpackShape, cus, (int64_t)D.rows, kUpWaves);
+  return launch("k_unpack", k_unpack, dim3(grid), dim3(kUpThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
                 row_src);
 }
 

@@ -124,21 +124,87 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float q) {
   return sign | (r - (120u << 3));
 }
 
+// ------------------------------------------------------------------ streaming rows
+//
+// The row kernels move gigabytes once, so every bulk access is a 16-byte
+// non-temporal load or store, and every workgroup streams its own contiguous
+// range of rows or tokens: on MI355X a workgroup-contiguous stream sustains
+// ~5.9 TB/s of copy traffic where a fine grid-stride interleave of the same
+// accesses sustains ~5.4 TB/s.  Each kernel has its own launch shape (waves
+// per workgroup, workgroups per CU), measured on the combine-heavy workload.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+#ifndef MOE_NONTEMPORAL
+#define MOE_NONTEMPORAL 1
+#endif
+
+struct LaunchShape {
+  int waves;          // waves per workgroup
+  int blocks_per_cu;  // workgroups per CU in the grid
+  constexpr int threads() const { return waves * 64; }
+};
+#ifndef MOE_PACK_SHAPE
+#define MOE_PACK_SHAPE {4, 8}
+#endif
+#ifndef MOE_UNPACK_SHAPE
+#define MOE_UNPACK_SHAPE {16, 1}
+#endif
+#ifndef MOE_COMB_SEND_SHAPE
+#define MOE_COMB_SEND_SHAPE {16, 1}
+#endif
+#ifndef MOE_COMB_RECV_SHAPE
+#define MOE_COMB_RECV_SHAPE {4, 4}
+#endif
+constexpr LaunchShape kPackShape = MOE_PACK_SHAPE;
+constexpr LaunchShape kUnpackShape = MOE_UNPACK_SHAPE;
+constexpr LaunchShape kCombSendShape = MOE_COMB_SEND_SHAPE;
+constexpr LaunchShape kCombRecvShape = MOE_COMB_RECV_SHAPE;
+constexpr LaunchShape kCopyShape = {16, 1};
+
+// Grid of a streaming kernel of shape S over `items` work units, at most
+// `per_block` of which a workgroup needs to be worth launching.
+inline int stream_grid(LaunchShape S, int cus, int64_t items, int64_t per_block) {
+  const int64_t need = (items + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)cus * S.blocks_per_cu;
+  return (int)(need < 1 ? 1 : (need < cap ? need : cap));
+}
+
+__device__ __forceinline__ v4u ld16(const v4u* p) {
+#if MOE_NONTEMPORAL
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ void st16(v4u* p, v4u v) {
+#if MOE_NONTEMPORAL
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// This workgroup's share [lo, hi) of n items split evenly over the grid.
+__device__ __forceinline__ void block_range(int n, int& lo, int& hi) {
+  lo = (int)((int64_t)n * blockIdx.x / gridDim.x);
+  hi = (int)((int64_t)n * (blockIdx.x + 1) / gridDim.x);
+}
+
 // Copy n16 16-byte units from src to dst with the whole wave; each lane
 // issues up to U loads before its stores.
 template <int U>
-__device__ __forceinline__ void wave_copy16(uint4* __restrict__ dst, const uint4* __restrict__ src, int n16, int lane) {
+__device__ __forceinline__ void wave_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src, int n16, int lane) {
   for (int c0 = 0; c0 < n16; c0 += kWave * U) {
-    uint4 r[U];
+    v4u r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave + lane;
-      r[u] = c < n16 ? src[c] : make_uint4(0, 0, 0, 0);
+      r[u] = c < n16 ? ld16(src + c) : v4u{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave + lane;
-      if (c < n16) dst[c] = r[u];
+      if (c < n16) st16(dst + c, r[u]);
     }
   }
 }
@@ -156,14 +222,14 @@ __device__ __forceinline__ int floor_index(const int* a, int n, int v, int strid
 // Launchers (one per translation unit that owns the kernels).
 int launch_route(const Dims& D, const Ws& W, const int* idx, int* send_pos, hipStream_t st);
 int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
-                float* recv_s, int grid, hipStream_t st);
+                float* recv_s, int cus, hipStream_t st);
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
-                  int* exp_off, int* row_src, int grid, hipStream_t st);
-int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int grid,
+                  int* exp_off, int* row_src, int cus, hipStream_t st);
+int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,
                      hipStream_t st);
-int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int grid,
+int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st);
-int launch_copy(void* dst, const void* src, int64_t n16, int grid, hipStream_t st);
+int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 
 }  // namespace moe
