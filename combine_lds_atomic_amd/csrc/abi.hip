@@ -41,7 +41,17 @@ int make_dims(const moe_shape* sh, Dims* D) {
   D->k = s.k;
   D->L = s.E / s.N;
   D->TK = (int)tk;
-  D->B = (int)((tk + kChunk - 1) / kChunk);
+  // A rank that fits one chunk (<= 4096 slots) gets exactly one, so the count
+  // kernel finishes its positions; larger ranks get the smallest power-of-two
+  // chunk (256..4096 slots) that keeps their chunks at 32 or fewer.
+  int C = kMinChunk;
+  if (tk <= kMaxChunk) {
+    while (C < tk) C *= 2;
+  } else {
+    while (C < kMaxChunk && (tk + C - 1) / C > 32) C *= 2;
+  }
+  D->C = C;
+  D->B = (int)((tk + C - 1) / C);
   D->NB = s.H / kScaleBlock;
   D->R = (int)s.region_rows;
   D->rows = (int)rows;
@@ -63,7 +73,6 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   };
   char* hdr = take(kAlign);
   W->err = reinterpret_cast<uint32_t*>(hdr);
-  W->ticket = reinterpret_cast<uint32_t*>(hdr ? hdr + 64 : nullptr);
   W->blk = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * D.B * D.E));
   W->cnt = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * D.E));
   W->send_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.E + 1)));

@@ -62,16 +62,20 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
   block_range(D.N * D.T, lo, hi);
   for (int tok = lo + wv; tok < hi; tok += kPkWaves) {
     const int s = tok / D.T, t = tok - s * D.T;
-    // Lane j < k resolves slot j: position = chunk base of its expert + rank
-    // inside the chunk (left in send_pos by the count kernel).
+    // Lane j < k resolves slot j.  With one routing chunk per rank the count
+    // kernel already wrote the final position; otherwise it left the rank
+    // inside the chunk, and the chunk's base for the expert completes it.
     int row = -1;
     if (lane < D.k) {
       const int i = t * D.k + lane;
       const int64_t slot = (int64_t)s * D.TK + i;
       const int e = idx[slot];
       if (e >= 0 && e < D.E) {
-        const int sp = W.blk[((int64_t)s * D.B + i / kChunk) * D.E + e] + send_pos[slot];
-        send_pos[slot] = sp;
+        int sp = send_pos[slot];
+        if (D.B > 1) {
+          sp += W.blk[((int64_t)s * D.B + i / D.C) * D.E + e];
+          send_pos[slot] = sp;
+        }
         const int d = e / D.L;
         const int r = W.recv_off[d * (D.N + 1) + s] + sp - W.send_off[s * (D.E + 1) + d * D.L];
         const int pr = W.base[d] + r;

@@ -5,16 +5,56 @@
 //
 // The pages count in one block with shared-memory atomics, copy the counts to
 // the host and compute the receive-side offsets on the CPU.  Here every rank's
-// counts are already in HBM, so the whole exchange is two kernels:
+// counts are already in HBM, so the whole exchange is two or three short
+// kernels:
 //   k_route_count  grid (chunks, N): LDS-atomic occupancy masks per 64-slot
 //                  batch give per-expert counts and stable in-chunk ranks;
-//   k_route_scan   grid (N): per-rank scans over chunks and experts; the last
-//                  block to arrive (ticket) runs the cross-rank scans.
+//                  when a rank's slots fit one chunk it also does that rank's
+//                  scan, and the positions it writes are final;
+//   k_route_scan   grid (N), only with several chunks per rank: per-rank
+//                  scans over chunks and experts;
+//   k_route_cross  one block: the cross-rank scans (receive offsets, expert
+//                  offsets, region bases) and the capacity / bound checks.
+// Kernel boundaries order the three; no grid-wide fence is needed (on a
+// multi-XCD GPU an agent-scope fence costs a write-back of the L2).
 #include "moe_internal.h"
 
 namespace moe {
 
-// Counts and in-chunk ranks of one chunk of kChunk slots of rank s.
+// Exclusive scan of one value per thread over a block of THREADS threads.
+// Returns the thread's exclusive prefix; *total gets the block total.
+// wsum: LDS scratch of THREADS/64 + 1 ints.
+template <int THREADS>
+__device__ int block_scan(int v, int* wsum, int* total) {
+  constexpr int kW = THREADS / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < kW ? wsum[lane] : 0;
+    int u = t;
+#pragma unroll
+    for (int d = 1; d < kW; d <<= 1) {
+      const int y = __shfl_up(u, d);
+      if (lane >= d) u += y;
+    }
+    if (lane < kW) wsum[lane] = u - t;         // exclusive wave offsets
+    if (lane == kW - 1) wsum[kW] = u;          // block total
+  }
+  __syncthreads();
+  const int r = wsum[w] + x - v;
+  *total = wsum[kW];
+  __syncthreads();
+  return r;
+}
+
+// Counts and in-chunk ranks of one chunk of D.C slots of rank s.
 //
 // Each wave walks its quarter of the chunk 64 slots at a time.  Lane i ORs
 // bit i into an LDS mask of its expert (ds_or_b64: one LDS atomic per slot);
@@ -25,36 +65,45 @@ namespace moe {
 // which makes the final positions unique and reproducible.
 __global__ __launch_bounds__(kThreads) void k_route_count(Dims D, Ws W, const int* __restrict__ idx,
                                                           int* __restrict__ send_pos) {
-  extern __shared__ unsigned char smem[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);   // [4][E]
   int* run = reinterpret_cast<int*>(mask + kWavesPerBlock * D.E);            // [4][E]
+  __shared__ int wsum[kWavesPerBlock + 1];
   const int s = blockIdx.y, b = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  if (s == 0 && b == 0 && threadIdx.x == 0) *W.ticket = 0;   // the scan kernel runs after this one
   for (int i = threadIdx.x; i < kWavesPerBlock * D.E; i += kThreads) {
     mask[i] = 0ull;
     run[i] = 0;
   }
-  __syncthreads();
 
   const int64_t rbase = (int64_t)s * D.TK;
-  const int c0 = b * kChunk + w * kPerWave;
-  const int cend = min(c0 + kPerWave, D.TK);
-  unsigned long long* wm = mask + w * D.E;
-  int* wr = run + w * D.E;
-  int ev[kBatches], rv[kBatches];
+  const int per_wave = D.C / kWavesPerBlock;
+  const int c0 = b * D.C + w * per_wave;
+  const int cend = min(c0 + per_wave, D.TK);
+  // All of this wave's ids are loaded before any LDS work.
+  int ev[kMaxBatches], rv[kMaxBatches];
   bool bad = false;
 #pragma unroll
-  for (int bt = 0; bt < kBatches; ++bt) {
+  for (int bt = 0; bt < kMaxBatches; ++bt) {
     const int i = c0 + bt * kWave + lane;
     int e = -1;
-    if (i < cend) {
+    if (bt * kWave < per_wave && i < cend) {
       e = idx[rbase + i];
       if (e < 0 || e >= D.E) {
         bad = true;
         e = -1;
       }
     }
+    ev[bt] = e;
+  }
+  __syncthreads();
+
+  unsigned long long* wm = mask + w * D.E;
+  int* wr = run + w * D.E;
+#pragma unroll
+  for (int bt = 0; bt < kMaxBatches; ++bt) {
+    if (bt * kWave >= per_wave) break;
+    const int e = ev[bt];
     if (e >= 0) atomicOr(&wm[e], 1ull << lane);
     __builtin_amdgcn_wave_barrier();
     unsigned long long m = 0ull;
@@ -69,15 +118,17 @@ __global__ __launch_bounds__(kThreads) void k_route_count(Dims D, Ws W, const in
       wm[e] = 0ull;
     }
     __builtin_amdgcn_wave_barrier();
-    ev[bt] = e;
     rv[bt] = r;
   }
   if (__any(bad) && lane == 0) atomicOr(W.err, MOE_FLAG_BADID);
   __syncthreads();
 
-  // Exclusive prefix over the four waves, per expert, and the chunk totals.
-  int* blk = W.blk + ((int64_t)s * D.B + b) * D.E;
-  for (int e = threadIdx.x; e < D.E; e += kThreads) {
+  // Exclusive prefix over the four waves, per expert; the chunk totals go to
+  // the workspace.  Thread t owns experts [t*per, t*per + per).
+  const int per = (D.E + kThreads - 1) / kThreads;
+  const int e0 = min(D.E, (int)threadIdx.x * per), e1 = min(D.E, e0 + per);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) {
     int p = 0;
 #pragma unroll
     for (int ww = 0; ww < kWavesPerBlock; ++ww) {
@@ -85,131 +136,279 @@ __global__ __launch_bounds__(kThreads) void k_route_count(Dims D, Ws W, const in
       run[ww * D.E + e] = p;
       p += c;
     }
-    blk[e] = p;
+    if (D.B > 1) W.blk[((int64_t)s * D.B + b) * D.E + e] = p;
+    else W.cnt[s * D.E + e] = p;
+    mask[e] = (unsigned long long)p;       // masks are all clear again: reuse as scratch
+    mine += p;
+  }
+  if (D.B == 1) {
+    // The whole rank is this chunk: its scan over experts makes the
+    // positions final here.
+    int total;
+    int off = block_scan<kThreads>(mine, wsum, &total);
+    int* so = W.send_off + s * (D.E + 1);
+    for (int e = e0; e < e1; ++e) {
+      so[e] = off;
+#pragma unroll
+      for (int ww = 0; ww < kWavesPerBlock; ++ww) run[ww * D.E + e] += off;
+      off += (int)mask[e];
+    }
+    if (threadIdx.x == 0) so[D.E] = total;
   }
   __syncthreads();
 #pragma unroll
-  for (int bt = 0; bt < kBatches; ++bt) {
+  for (int bt = 0; bt < kMaxBatches; ++bt) {
+    if (bt * kWave >= per_wave) break;
     const int i = c0 + bt * kWave + lane;
     if (i < cend) send_pos[rbase + i] = ev[bt] >= 0 ? wr[ev[bt]] + rv[bt] : -1;
   }
 }
 
-// Exclusive scan of v[0..n) in LDS by one 256-thread block; returns the total.
-__device__ int block_excl_scan(int* v, int n, int* part) {
-  const int tid = threadIdx.x;
-  const int per = (n + kThreads - 1) / kThreads;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += v[i];
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < kThreads; ++i) {
-      const int c = part[i];
-      part[i] = acc;
-      acc += c;
-    }
-    part[kThreads] = acc;
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / kWave;
+
+// Sum of get(s) for s in [s0, s1), the loads issued eight at a time.
+template <typename Get>
+__device__ __forceinline__ int sum_range(int s0, int s1, Get get) {
+  int acc = 0;
+  int s = s0;
+  for (; s + 8 <= s1; s += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = get(s + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
   }
-  __syncthreads();
-  int acc = part[tid];
-  for (int i = lo; i < hi; ++i) {
-    const int c = v[i];
-    v[i] = acc;
-    acc += c;
-  }
-  const int total = part[kThreads];
-  __syncthreads();
-  return total;
+  for (; s < s1; ++s) acc += get(s);
+  return acc;
 }
 
-// Per-rank scans (block s), then -- in the last block to finish -- the scans
-// across ranks that the receive side needs.
-__global__ __launch_bounds__(kThreads) void k_route_scan(Dims D, Ws W) {
-  __shared__ int sv[kMaxE + 1];
-  __shared__ int part[kThreads + 1];
-  __shared__ int srt[kMaxN];
-  __shared__ int last;
+// put(s, exclusive prefix) for s in [s0, s1), starting from acc; loads issued
+// eight at a time.
+template <typename Get, typename Put>
+__device__ __forceinline__ void scan_range(int s0, int s1, int acc, Get get, Put put) {
+  int s = s0;
+  for (; s + 8 <= s1; s += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = get(s + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      put(s + u, acc);
+      acc += v[u];
+    }
+  }
+  for (; s < s1; ++s) {
+    const int v = get(s);
+    put(s, acc);
+    acc += v;
+  }
+}
+
+// Per-rank scans over chunks and experts (block s), when a rank has several
+// chunks: chunk counts become chunk base positions.
+__global__ __launch_bounds__(kScanThreads) void k_route_scan(Dims D, Ws W) {
+  __shared__ int wsum[kScanWaves + 1];
   const int s = blockIdx.x, tid = threadIdx.x;
-
-  // Totals per expert; chunk counts become exclusive prefixes over chunks.
-  for (int e = tid; e < D.E; e += kThreads) {
-    int acc = 0;
-    for (int b = 0; b < D.B; ++b) {
-      int* p = W.blk + ((int64_t)s * D.B + b) * D.E + e;
-      const int c = *p;
-      *p = acc;
-      acc += c;
+  const int E = D.E;
+  // One expert per thread (E <= 1024), its chunk counts loaded four at a time.
+  int tot = 0;
+  if (tid < E) {
+    int* p = W.blk + (int64_t)s * D.B * E + tid;
+    int b = 0;
+    for (; b + 4 <= D.B; b += 4) {
+      const int c0 = p[(int64_t)b * E], c1 = p[(int64_t)(b + 1) * E], c2 = p[(int64_t)(b + 2) * E],
+                c3 = p[(int64_t)(b + 3) * E];
+      p[(int64_t)b * E] = tot;
+      p[(int64_t)(b + 1) * E] = tot + c0;
+      p[(int64_t)(b + 2) * E] = tot + c0 + c1;
+      p[(int64_t)(b + 3) * E] = tot + c0 + c1 + c2;
+      tot += c0 + c1 + c2 + c3;
     }
-    sv[e] = acc;
-    W.cnt[s * D.E + e] = acc;
+    for (; b < D.B; ++b) {
+      const int c = p[(int64_t)b * E];
+      p[(int64_t)b * E] = tot;
+      tot += c;
+    }
+    W.cnt[s * E + tid] = tot;
   }
-  __syncthreads();
-  const int total = block_excl_scan(sv, D.E, part);
-  int* so = W.send_off + s * (D.E + 1);
-  for (int e = tid; e < D.E; e += kThreads) {
-    so[e] = sv[e];
-    for (int b = 0; b < D.B; ++b) W.blk[((int64_t)s * D.B + b) * D.E + e] += sv[e];
+  int total;
+  const int off = block_scan<kScanThreads>(tid < E ? tot : 0, wsum, &total);
+  int* so = W.send_off + s * (E + 1);
+  if (tid < E) {
+    so[tid] = off;
+    int* p = W.blk + (int64_t)s * D.B * E + tid;
+    for (int b = 0; b < D.B; ++b) p[(int64_t)b * E] += off;
   }
-  if (tid == 0) so[D.E] = total;
+  if (tid == 0) so[E] = total;
+}
 
-  // Release this block's tables device-wide, then take a ticket.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(W.ticket, 1u) == (unsigned)(D.N - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+// Largest N*E whose count table the cross-rank kernel stages in LDS (96 KB),
+// and the largest N for which the N x N rank-to-rank counts stay in
+// registers while that table is reused for them.
+constexpr int kCrossTable = 24576;
+constexpr int kCrossMaxN = 128;
 
+// The scans across ranks that the receive side needs; one block.
+__global__ __launch_bounds__(kScanThreads) void k_route_cross(Dims D, Ws W) {
+  __shared__ int tab[kCrossTable];
+  __shared__ int ex[kMaxE + 1];
+  __shared__ int rt[kMaxN];
+  __shared__ int wsum[kScanWaves + 1];
+  const int tid = threadIdx.x;
   const int N = D.N, E = D.E, L = D.L;
-  // Rows from each source into each destination, stacked by source.
-  for (int d = tid; d < N; d += kThreads) {
-    int acc = 0;
-    for (int s2 = 0; s2 < N; ++s2) {
-      W.recv_off[d * (N + 1) + s2] = acc;
-      const int* o = W.send_off + s2 * (E + 1);
-      acc += o[(d + 1) * L] - o[d * L];
+
+  if (N * E <= kCrossTable && N <= kCrossMaxN) {
+    // Stage cnt[N][E] (coalesced, eight loads in flight per thread).
+    const int n = N * E;
+    for (int i0 = tid; i0 < n; i0 += kScanThreads * 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kScanThreads;
+        v[u] = i < n ? W.cnt[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kScanThreads;
+        if (i < n) tab[i] = v[u];
+      }
     }
-    W.recv_off[d * (N + 1) + N] = acc;
-    W.recv_total[d] = acc;
-    srt[d] = acc;
+    __syncthreads();
+    // (1) src_in_exp[s][e] = rows of expert e from sources before s.
+    for (int e = tid; e < E; e += kScanThreads) {
+      int acc = 0;
+      for (int s = 0; s < N; ++s) {
+        W.src_in_exp[s * E + e] = acc;
+        acc += tab[s * E + e];
+      }
+      W.src_in_exp[N * E + e] = acc;
+      ex[e] = acc;
+    }
+    // (3a) c[s][d] = rows from source s to destination d, kept in registers
+    // while the table is rewritten as c.
+    constexpr int kCPer = kCrossMaxN * kCrossMaxN / kScanThreads;
+    int cv[kCPer];
+#pragma unroll
+    for (int u = 0; u < kCPer; ++u) {
+      const int i = tid + u * kScanThreads;   // i = s * N + d
+      int c = 0;
+      if (i < N * N) {
+        const int s = i / N, d = i - s * N;
+        for (int l = 0; l < L; ++l) c += tab[s * E + d * L + l];
+      }
+      cv[u] = c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCPer; ++u) {
+      const int i = tid + u * kScanThreads;
+      if (i < N * N) tab[i] = cv[u];
+    }
+    __syncthreads();
+    // (3b) recv_off[d][s] = rows from sources before s, stacked by source.
+    for (int d = tid; d < N; d += kScanThreads) {
+      int acc = 0;
+      for (int s = 0; s < N; ++s) {
+        W.recv_off[d * (N + 1) + s] = acc;
+        acc += tab[s * N + d];
+      }
+      W.recv_off[d * (N + 1) + N] = acc;
+      W.recv_total[d] = acc;
+      rt[d] = acc;
+    }
+    __syncthreads();
+  } else {
+    // General shapes: the same scans from global memory, the sources split
+    // over G thread groups per column.
+    int* part = tab;
+    {
+      const int G = min(N, max(1, kScanThreads / E));
+      const int e = tid % E, g = tid / E;
+      const bool mine = tid < G * E;
+      const int per = (N + G - 1) / G;
+      const int s0 = min(N, g * per), s1 = min(N, s0 + per);
+      const int* cnt = W.cnt;
+      auto get = [&](int s2) { return cnt[s2 * E + e]; };
+      if (mine) part[g * E + e] = sum_range(s0, s1, get);
+      __syncthreads();
+      for (int e2 = tid; e2 < E; e2 += kScanThreads) {
+        int a = 0;
+        for (int g2 = 0; g2 < G; ++g2) {
+          const int c = part[g2 * E + e2];
+          part[g2 * E + e2] = a;
+          a += c;
+        }
+        ex[e2] = a;
+        W.src_in_exp[N * E + e2] = a;
+      }
+      __syncthreads();
+      int* sie = W.src_in_exp;
+      if (mine) scan_range(s0, s1, part[g * E + e], get, [&](int s2, int v) { sie[s2 * E + e] = v; });
+      __syncthreads();
+    }
+    {
+      const int G = min(N, max(1, kScanThreads / N));
+      const int d = tid % N, g = tid / N;
+      const bool mine = tid < G * N;
+      const int per = (N + G - 1) / G;
+      const int s0 = min(N, g * per), s1 = min(N, s0 + per);
+      const int* so_all = W.send_off;
+      auto get = [&](int s2) {
+        const int* o = so_all + s2 * (E + 1);
+        return o[(d + 1) * L] - o[d * L];
+      };
+      if (mine) part[g * N + d] = sum_range(s0, s1, get);
+      __syncthreads();
+      for (int d2 = tid; d2 < N; d2 += kScanThreads) {
+        int a = 0;
+        for (int g2 = 0; g2 < G; ++g2) {
+          const int c = part[g2 * N + d2];
+          part[g2 * N + d2] = a;
+          a += c;
+        }
+        W.recv_off[d2 * (N + 1) + N] = a;
+        W.recv_total[d2] = a;
+        rt[d2] = a;
+      }
+      __syncthreads();
+      int* ro = W.recv_off + d * (N + 1);
+      if (mine) scan_range(s0, s1, part[g * N + d], get, [&](int s2, int v) { ro[s2] = v; });
+      __syncthreads();
+    }
   }
-  // Rows of expert e contributed by earlier sources, and expert totals.
-  for (int e = tid; e < E; e += kThreads) {
-    int acc = 0;
-    for (int s2 = 0; s2 < N; ++s2) {
-      W.src_in_exp[s2 * E + e] = acc;
-      acc += W.cnt[s2 * E + e];
+  // (2) exp_off[d][l] from one exclusive scan over all experts.
+  {
+    int etot;
+    const int x = block_scan<kScanThreads>(tid < E ? ex[tid] : 0, wsum, &etot);
+    __syncthreads();
+    if (tid < E) ex[tid] = x;
+    if (tid == 0) ex[E] = etot;
+    __syncthreads();
+    for (int i = tid; i < N * (L + 1); i += kScanThreads) {
+      const int d = i / (L + 1), l = i - d * (L + 1);
+      W.exp_off[i] = ex[d * L + l] - ex[d * L];
     }
-    W.src_in_exp[N * E + e] = acc;
-    sv[e] = acc;
   }
-  __syncthreads();
-  for (int d = tid; d < N; d += kThreads) {
-    int acc = 0;
-    for (int l = 0; l < L; ++l) {
-      W.exp_off[d * (L + 1) + l] = acc;
-      acc += sv[d * L + l];
+  // (4) Region bases and rows written per region; capacity and bound checks.
+  {
+    const int r = tid < N ? rt[tid] : 0;
+    const int used = D.R ? min(r, D.R) : r;
+    int all, vall;
+    const int b = block_scan<kScanThreads>(r, wsum, &all);
+    const int vb = block_scan<kScanThreads>(used, wsum, &vall);
+    if (tid < N) {
+      W.base[tid] = D.R ? tid * D.R : b;
+      W.vprefix[tid] = vb;
+      uint32_t fl = 0;
+      if (D.R && r > D.R) fl |= MOE_FLAG_OVERFLOW;
+      if ((int64_t)r > D.bound) fl |= MOE_FLAG_BOUND;
+      if (fl) atomicOr(W.err, fl);
     }
-    W.exp_off[d * (L + 1) + L] = acc;
-  }
-  if (tid == 0) {
-    int64_t acc = 0, vacc = 0;
-    uint32_t fl = 0;
-    for (int d = 0; d < N; ++d) {
-      const int tot = srt[d];
-      W.base[d] = D.R ? d * D.R : (int)acc;
-      W.vprefix[d] = (int)vacc;
-      vacc += D.R ? min(tot, D.R) : tot;
-      acc += tot;
-      if (D.R && tot > D.R) fl |= MOE_FLAG_OVERFLOW;
-      if ((int64_t)tot > D.bound) fl |= MOE_FLAG_BOUND;
+    if (tid == 0) {
+      W.base[N] = D.R ? N * D.R : all;
+      W.vprefix[N] = vall;
     }
-    W.base[N] = D.R ? N * D.R : (int)acc;
-    W.vprefix[N] = (int)vacc;
-    if (fl) atomicOr(W.err, fl);
   }
 }
 
@@ -220,12 +419,12 @@ int launch_route(const Dims& D, const Ws& W, const int* idx, int* send_pos, hipS
     const size_t lds = (size_t)kWavesPerBlock * D.E * (sizeof(unsigned long long) + sizeof(int));
     const int rc = launch("k_route_count", k_route_count, dim3(D.B, D.N), dim3(kThreads), lds, st, D, W, idx, send_pos);
     if (rc != MOE_OK) return rc;
-  } else {
-    // No slots: the scan still publishes zero counts; reset the ticket.
-    const int rc = launch_fill_u32(W.ticket, 0u, 1, st);
+  }
+  if (D.B != 1) {   // several chunks per rank (or none): per-rank scans
+    const int rc = launch("k_route_scan", k_route_scan, dim3(D.N), dim3(kScanThreads), 0, st, D, W);
     if (rc != MOE_OK) return rc;
   }
-  return launch("k_route_scan", k_route_scan, dim3(D.N), dim3(kThreads), 0, st, D, W);
+  return launch("k_route_cross", k_route_cross, dim3(1), dim3(kScanThreads), 0, st, D, W);
 }
 
 }  // namespace moe

@@ -42,16 +42,19 @@ constexpr int kMaxH = 32768;
 constexpr int kScaleBlock = 128;     // elements per fp32 scale
 constexpr int kMaxNB = kMaxH / kScaleBlock;
 // Routing chunk: slots of one rank handled by one workgroup of the count
-// kernel; every wave takes a contiguous quarter, 64 slots per batch.
-constexpr int kChunk = 4096;
-constexpr int kPerWave = kChunk / kWavesPerBlock;
-constexpr int kBatches = kPerWave / kWave;
+// kernel; every wave takes a contiguous quarter, 64 slots per batch.  The
+// chunk is 256..4096 slots, chosen per shape so that small batches still
+// spread over several workgroups per rank.
+constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 4096;
+constexpr int kMaxBatches = kMaxChunk / kWavesPerBlock / kWave;
 
 // Problem sizes derived once on the host.
 struct Dims {
   int N, T, H, E, k;
   int L;        // experts per rank
   int TK;       // slots per rank = T*k
+  int C;        // routing chunk, slots
   int B;        // routing chunks per rank
   int NB;       // scale blocks per row = H/128
   int R;        // fixed region rows, 0 = packed
@@ -62,7 +65,6 @@ struct Dims {
 // Workspace tables, all int32 unless noted.
 struct Ws {
   uint32_t *err;      // sticky MOE_FLAG_* word
-  uint32_t *ticket;   // arrivals of the per-rank scan blocks
   int *blk;           // [N][B][E] chunk counts, then chunk base positions
   int *cnt;           // [N][E]
   int *send_off;      // [N][E+1]

@@ -96,10 +96,10 @@ int64_t moe_recv_rows(const moe_shape *shape);
 
 /* Bytes of workspace the calls need for `shape` (negative MOE_E* if rejected).
  * The workspace holds per-chunk and per-rank counts, all offsets, the region
- * bases, a ticket counter and the sticky error word. */
+ * bases and the sticky error word. */
 int64_t moe_workspace_bytes(const moe_shape *shape);
 
-/* Zero the workspace header (error word and ticket).  Call once after
+/* Zero the workspace header (the error word).  Call once after
  * allocating a workspace, before its first use.  ws: device, 256-B aligned. */
 int moe_workspace_init(const moe_shape *shape, void *ws, void *stream);
 

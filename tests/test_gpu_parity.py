@@ -60,14 +60,15 @@ def test_literal_bound_regions():
 
 
 @pytest.mark.parametrize("N,T,H,E,k", [
-    (3, 1500, 384, 12, 3),      # two routing chunks, ragged; 3 scale blocks per row
-    (8, 512, 640, 64, 8),       # exactly one full chunk (T*k = 4096)
-    (8, 513, 1152, 64, 8),      # one slot past a chunk; 9 scale blocks
+    (3, 1500, 384, 12, 3),      # 18 routing chunks, ragged last one; 3 scale blocks per row
+    (8, 512, 640, 64, 8),       # T*k = 4096: whole chunks only
+    (8, 513, 1152, 64, 8),      # 8 slots past whole chunks; 9 scale blocks
     (1, 1, 128, 1, 1),          # one rank, one token, one expert
     (4, 5, 128, 4, 1),          # E = N, k = 1
     (8, 33, 256, 16, 8),        # k > E/N: the bound uses k
     (2, 0, 256, 8, 2),          # no tokens
     (5, 77, 9216, 40, 6),       # H above one 1024-element wave pass, ragged
+    (2, 20000, 128, 8, 8),      # 40 chunks of 4096 slots per rank
 ])
 def test_shapes(N, T, H, E, k):
     cfg = _small(f"s{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k)
