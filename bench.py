@@ -5,6 +5,14 @@ positions, quantise + pack), moe_dispatch_recv (expert-major unpack),
 moe_combine_send and moe_combine_recv, for all N logical ranks.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints one JSON line.
 
+Workloads whose combine batch differs from the dispatch batch (the Kimi-K2
+shape: dispatch 128, combine 4096 tokens per rank) time the dispatch at the
+dispatch batch and the combine on the layout of an untimed, payload-free
+dispatch at the combine batch.
+
+The pulling combine (moe_combine_pull) is timed after the steps, on the same
+data, and reported beside them; it is not part of the step.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -20,18 +28,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+PHASES = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
+KERNEL_OF = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
+             "combine_recv": "k_comb_recv"}
 
 
-def algorithmic_bytes(N, T, H, E, k):
-    """Bytes each phase must move (inputs read once, outputs written once)."""
-    P = N * T * k
+def algorithmic_bytes(N, T, H, E, k, Tc=None):
+    """Bytes each phase must move (inputs read once, outputs written once);
+    Tc is the combine batch when it differs from the dispatch batch T."""
+    Tc = T if Tc is None else Tc
+    P, Pc = N * T * k, N * Tc * k
     rowq = H + 4 * (H // 128)          # fp8 payload + fp32 scales
     rowb = 2 * H                       # bf16 row
     return {
         "dispatch_send": N * T * 2 * H + P * rowq + 2 * N * T * k * 4 + N * E * 4,
         "dispatch_recv": 2 * P * rowq,
-        "combine_send": 2 * P * rowb,
-        "combine_recv": P * rowb + N * T * H * 2 + 2 * N * T * k * 4,
+        "combine_send": 2 * Pc * rowb,
+        "combine_recv": Pc * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
+        "combine_pull": Pc * rowb + N * Tc * H * 2 + 3 * N * Tc * k * 4,
     }
 
 
@@ -78,7 +92,8 @@ def cpu_baseline(T_sample: int):
     O.combine_recv(comb, lay.send_pos, w, T_sample, cfg.k)
     t3 = time.perf_counter()
     sec = (t1 - t0) + (t3 - t2)
-    nbytes = sum(algorithmic_bytes(cfg.N, T_sample, cfg.H, cfg.E, cfg.k).values())
+    nb = algorithmic_bytes(cfg.N, T_sample, cfg.H, cfg.E, cfg.k)
+    nbytes = sum(nb[p] for p in PHASES)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(sec, 2),
             "sample": f"combine_heavy shape with T={T_sample} tokens/rank (N={cfg.N}, H={cfg.H}, E={cfg.E}, "
@@ -107,21 +122,30 @@ def main():
     import workloads as W
 
     cfg = W.CONFIGS[args.workload]
-    T = cfg.Tc if cfg.T_comb else cfg.T
-    if cfg.T_comb and cfg.T_comb != cfg.T:
-        raise SystemExit("bench.py times workloads whose dispatch and combine batches match")
+    T, Tc = cfg.T, cfg.Tc
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # Dispatch problem (timed) at batch T.
     sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k)
     idx, w = W.routing(cfg, T)
     idx_d = torch.from_numpy(idx).to(dev)
-    w_d = torch.from_numpy(w).to(dev)
     x = W.tokens(cfg, dev, T)
-    B = moe.allocate(sh, dev)
-    y = W.expert_outputs(cfg, B.rows, dev)
-    stream = torch.cuda.current_stream()
-
-    phases = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
+    B = moe.allocate(sh, dev, combine=(Tc == T))
+    # Combine problem at batch Tc: the same buffers when Tc == T, otherwise the
+    # layout of an untimed, payload-free dispatch at Tc.
+    if Tc == T:
+        shc, Bc, idxc_d, wc_d = sh, B, idx_d, torch.from_numpy(w).to(dev)
+    else:
+        shc = moe.shape(cfg.N, Tc, cfg.H, cfg.E, cfg.k)
+        idxc, wc = W.routing(cfg, Tc)
+        idxc_d, wc_d = torch.from_numpy(idxc).to(dev), torch.from_numpy(wc).to(dev)
+        Bc = moe.allocate(shc, dev, payload=False)
+        moe.moe_dispatch_send(shc, None, idxc_d, None, None, Bc.send_pos, Bc.ws)
+        moe.moe_dispatch_recv(shc, None, None, Bc.ws, None, None, Bc.exp_off, Bc.row_src)
+    y = W.expert_outputs(cfg, Bc.rows, dev)
+    out_pull = torch.empty_like(Bc.out)
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -129,15 +153,15 @@ def main():
         if ev: ev[1].record(stream)
         moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
         if ev: ev[2].record(stream)
-        moe.moe_combine_send(sh, y, B.row_src, B.ws, B.comb)
+        moe.moe_combine_send(shc, y, Bc.row_src, Bc.ws, Bc.comb)
         if ev: ev[3].record(stream)
-        moe.moe_combine_recv(sh, B.comb, B.send_pos, w_d, B.out)
+        moe.moe_combine_recv(shc, Bc.comb, Bc.send_pos, wc_d, Bc.out)
         if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    flags = moe.moe_status(B.ws)
+    flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
         raise SystemExit(f"device error flags {flags:#x} during warm-up")
 
@@ -153,12 +177,24 @@ def main():
     per_phase_ms = ms.mean(axis=0)
     p90_ms = np.percentile(ms, 90, axis=0)
     step_ms = wall * 1e3 / args.steps
-    nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k)
-    total = sum(nbytes.values())
+    nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k, Tc)
+    total = sum(nbytes[p] for p in PHASES)
+
+    # The pulling combine on the same data (not part of the step).
+    pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for _ in range(2):
+        moe.moe_combine_pull(shc, y, idxc_d, Bc.send_pos, wc_d, Bc.ws, out_pull)
+    pull_ev[0].record(stream)
+    for i in range(args.steps):
+        moe.moe_combine_pull(shc, y, idxc_d, Bc.send_pos, wc_d, Bc.ws, out_pull)
+        pull_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    pull_ms = np.array([pull_ev[i].elapsed_time(pull_ev[i + 1]) for i in range(args.steps)]).mean()
+    pull_same = bool(torch.equal(out_pull.view(torch.int16), Bc.out.view(torch.int16)))
 
     # Achievable read+write rate: a plain copy of the dominant phase's bytes.
     dom = max(range(4), key=lambda p: per_phase_ms[p])
-    copy_bytes = (nbytes[phases[dom]] // 2) // 16 * 16
+    copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
     src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(2):
@@ -172,20 +208,24 @@ def main():
     copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    flags = moe.moe_status(B.ws)
+    flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
         raise SystemExit(f"device error flags {flags:#x} in the timed steps")
 
-    phase_info = {}
-    for p, name in enumerate(phases):
-        gbs = nbytes[name] / (per_phase_ms[p] * 1e-3) / 1e9
-        phase_info[name] = {"us": round(per_phase_ms[p] * 1e3, 1), "p90_us": round(p90_ms[p] * 1e3, 1),
-                            "alg_bytes": nbytes[name], "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    dom_name = phases[dom]
+    def info(name, t_ms, t90=None):
+        gbs = nbytes[name] / (t_ms * 1e-3) / 1e9
+        d = {"us": round(t_ms * 1e3, 1), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
+             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if t90 is not None:
+            d["p90_us"] = round(t90 * 1e3, 1)
+        return d
+
+    phase_info = {name: info(name, per_phase_ms[p], p90_ms[p]) for p, name in enumerate(PHASES)}
+    dom_name = PHASES[dom]
     achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
-    kernel = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
-              "combine_recv": "k_comb_recv"}[dom_name]
+    kernel = KERNEL_OF[dom_name]
     value = total / (step_ms * 1e-3) / 1e9
+    batch = f"T={T}" if Tc == T else f"dispatch T={T}, combine T={Tc}"
     res = {
         "metric": "dispatch / combine us per layer and effective HBM GB/s (% of ~8 TB/s peak)",
         "value": round(value, 1),
@@ -199,12 +239,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.note}; packed receive regions", "N": cfg.N, "T": T, "H": cfg.H,
-                   "E": cfg.E, "k": cfg.k, "region_rows": 0, "payload": "bf16 in, e4m3fn+fp32 block-128 scales "
-                   "dispatched, bf16 combined with fp32 accumulation"},
+        "config": {"workload": f"{cfg.name}: {cfg.note}; packed receive regions", "N": cfg.N, "T": T, "T_comb": Tc,
+                   "H": cfg.H, "E": cfg.E, "k": cfg.k, "region_rows": 0, "batch": batch,
+                   "payload": "bf16 in, e4m3fn+fp32 block-128 scales dispatched, bf16 combined with fp32 accumulation"},
         "phases": phase_info,
         "dispatch_us": round((per_phase_ms[0] + per_phase_ms[1]) * 1e3, 1),
         "combine_us": round((per_phase_ms[2] + per_phase_ms[3]) * 1e3, 1),
+        "dispatch_frac": round((nbytes["dispatch_send"] + nbytes["dispatch_recv"]) /
+                               ((per_phase_ms[0] + per_phase_ms[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "combine_frac": round((nbytes["combine_send"] + nbytes["combine_recv"]) /
+                              ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

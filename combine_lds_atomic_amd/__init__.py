@@ -40,7 +40,7 @@ def shape(N: int, T: int, H: int, E: int, k: int, region_rows: int = 0) -> moe_s
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_lds_atomic_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python combine_lds_atomic_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 # torch ships its own HIP runtime.  It must be in the process before the
@@ -74,6 +74,7 @@ _SIG = {
     "moe_dispatch_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine_send": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "moe_combine_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
+    "moe_combine_pull": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
     "moe_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "moe_layout_export": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
     "moe_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
@@ -144,6 +145,11 @@ def moe_combine_send(sh, y_em, row_src, ws, comb, stream=None):
 def moe_combine_recv(sh, comb, send_pos, topk_w, out, stream=None):
     _check("moe_combine_recv", lib.moe_combine_recv(ctypes.byref(sh), _ptr(comb), _ptr(send_pos), _ptr(topk_w),
                                                     _ptr(out), _stream(stream)))
+
+
+def moe_combine_pull(sh, y_em, topk_idx, send_pos, topk_w, ws, out, stream=None):
+    _check("moe_combine_pull", lib.moe_combine_pull(ctypes.byref(sh), _ptr(y_em), _ptr(topk_idx), _ptr(send_pos),
+                                                    _ptr(topk_w), _ptr(ws), _ptr(out), _stream(stream)))
 
 
 def moe_status(ws, stream=None) -> int:

@@ -1,8 +1,10 @@
 """Build libmoe_ep.so (HIP, gfx950) in-tree with hipcc.
 
 Each .hip source is compiled to an object in parallel, then linked into
-``combine_lds_atomic_amd/libmoe_ep.so``.  Usage: ``python -m
-combine_lds_atomic_amd.build`` (or ``__graft_entry__.build()``).
+``combine_lds_atomic_amd/libmoe_ep.so``.  Usage: ``python
+combine_lds_atomic_amd/build.py`` (or ``__graft_entry__.build()``); run it by
+path, since importing the package needs a library that exports every
+declared symbol.
 """
 from __future__ import annotations
 

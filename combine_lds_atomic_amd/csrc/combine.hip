@@ -73,10 +73,14 @@ __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
 
 constexpr int kSlotGroup = 8;
 
-__global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, const uint16_t* __restrict__ comb,
-                                                           const int* __restrict__ send_pos,
-                                                           const float* __restrict__ topk_w,
-                                                           uint16_t* __restrict__ out) {
+// The weighted sum of one combine, token by token.  PULL = false: slot rows
+// are rank s's returned rows comb[s*T*k + send_pos].  PULL = true: they are
+// read where the expert wrote them, y_em[base[d] + expert-major index], found
+// from the routing tables (the row combine_send would have copied).
+template <bool PULL>
+__device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
+                                               const int* __restrict__ idx, const int* __restrict__ send_pos,
+                                               const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int lo, hi;
   block_range(D.N * D.T, lo, hi);
@@ -87,7 +91,20 @@ __global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, const uint16_t
     if (lane < D.k) {
       const int sp = send_pos[(int64_t)tok * D.k + lane];
       wt = topk_w[(int64_t)tok * D.k + lane];
-      if (sp >= 0 && sp < D.TK) row = s * D.TK + sp;
+      if (!PULL) {
+        if (sp >= 0 && sp < D.TK) row = s * D.TK + sp;
+      } else {
+        const int e = idx[(int64_t)tok * D.k + lane];
+        if (e >= 0 && e < D.E && sp >= 0 && sp < D.TK) {
+          const int d = e / D.L, l = e - d * D.L;
+          const int* so = W.send_off + s * (D.E + 1);
+          const int u = sp - so[e];                                          // index inside (s, e)
+          const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;   // expert-major
+          const int j = W.recv_off[d * (D.N + 1) + s] + (so[e] - so[d * D.L]) + u;     // source-major
+          const int p = W.base[d] + i;
+          if (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) row = p;
+        }
+      }
     }
     uint16_t* orow = out + (int64_t)tok * D.H;
     for (int col = lane * 8; col < D.H; col += kWave * 8) {
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, const uint16_t
         for (int jj = 0; jj < kSlotGroup; ++jj) {
           const int j = j0 + jj;
           rr[jj] = j < D.k ? __builtin_amdgcn_readlane(row, j) : -1;
-          v[jj] = rr[jj] >= 0 ? ld16(reinterpret_cast<const v4u*>(comb + (int64_t)rr[jj] * D.H + col))
+          v[jj] = rr[jj] >= 0 ? ld16(reinterpret_cast<const v4u*>(rows + (int64_t)rr[jj] * D.H + col))
                               : v4u{0, 0, 0, 0};
         }
 #pragma unroll
@@ -120,6 +137,21 @@ __global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, const uint16_t
       st16(reinterpret_cast<v4u*>(orow + col), o);
     }
   }
+}
+
+__global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, Ws W, const uint16_t* __restrict__ comb,
+                                                           const int* __restrict__ send_pos,
+                                                           const float* __restrict__ topk_w,
+                                                           uint16_t* __restrict__ out) {
+  combine_tokens<false>(D, W, comb, nullptr, send_pos, topk_w, out);
+}
+
+__global__ __launch_bounds__(kCrThreads) void k_comb_pull(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                           const int* __restrict__ idx,
+                                                           const int* __restrict__ send_pos,
+                                                           const float* __restrict__ topk_w,
+                                                           uint16_t* __restrict__ out) {
+  combine_tokens<true>(D, W, y, idx, send_pos, topk_w, out);
 }
 
 // Plain streaming copy: each workgroup copies one contiguous chunk.
@@ -149,7 +181,14 @@ int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, c
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_recv", k_comb_recv, dim3(grid), dim3(kCrThreads), 0, st, D, comb, send_pos, w, out);
+  return launch("k_comb_recv", k_comb_recv, dim3(grid), dim3(kCrThreads), 0, st, D, Ws{}, comb, send_pos, w, out);
+}
+
+int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
+                     const float* w, uint16_t* out, int cus, hipStream_t st) {
+  if (D.N * D.T == 0) return MOE_OK;
+  const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
+  return launch("k_comb_pull", k_comb_pull, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st) {

@@ -231,6 +231,8 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
                      hipStream_t st);
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st);
+int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
+                     const float* w, uint16_t* out, int cus, hipStream_t st);
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 

@@ -176,6 +176,26 @@ int moe_combine_recv(const moe_shape *shape, const uint16_t *comb, const int32_t
                      uint16_t *out, void *stream);
 
 /*
+ * Combine in one pass, pulling ("Dispatch and combine": peers whose buffers
+ * are mapped can pull tokens directly; on one GPU every rank is such a peer).
+ * Each source rank reads its slots' rows straight out of the expert-major
+ * outputs, so no combine_send copy is made:
+ *   out[s][t] = bf16_rne(sum_j w[s][t][j] * y_em[row of slot (s,t,j)]),
+ * the row found from the routing tables in ws (the same row moe_combine_send
+ * would copy), with the same float32 arithmetic and slot order as
+ * moe_combine_recv, hence the same bytes.  Slots without a row (bad id, or a
+ * fixed region that overflowed) contribute nothing.
+ *   y_em      bf16 [rows][H], 16-B aligned, expert-major (as for combine_send).
+ *   topk_idx  int32 [N][T][k], as given to moe_dispatch_send.
+ *   send_pos  int32 [N][T][k], from moe_dispatch_send.
+ *   topk_w    fp32 [N][T][k].
+ *   ws        the workspace of that dispatch.
+ *   out       bf16 [N][T][H] out, 16-B aligned.
+ */
+int moe_combine_pull(const moe_shape *shape, const uint16_t *y_em, const int32_t *topk_idx, const int32_t *send_pos,
+                     const float *topk_w, const void *ws, uint16_t *out, void *stream);
+
+/*
  * Wait for `stream`, return the sticky error bits accumulated in ws since the
  * last call (MOE_FLAG_*) through *flags, and clear them.  The only call that
  * blocks the host.

@@ -43,8 +43,12 @@ def run_all(cfg: W.Config, T: int, region_rows: int = 0, idx=None, w=None, x=Non
             B.comb.view(torch.int16).fill_(0x3F00)
         moe.moe_combine_send(sh, y, B.row_src, B.ws, B.comb)
         moe.moe_combine_recv(sh, B.comb, B.send_pos, w_d, B.out)
+        out_pull = torch.full_like(B.out, 7.0)
+        moe.moe_combine_pull(sh, y, idx_d, B.send_pos, w_d, B.ws, out_pull)
+    else:
+        out_pull = None
     flags = moe.moe_status(B.ws)
-    return dict(sh=sh, idx=np.asarray(idx), w=np.asarray(w), x=x, y=y, B=B, flags=flags)
+    return dict(sh=sh, idx=np.asarray(idx), w=np.asarray(w), x=x, y=y, B=B, flags=flags, out_pull=out_pull)
 
 
 def export_layout(r):
@@ -111,6 +115,7 @@ def check_full(r, lay: O.Layout, check_comb=True):
         out = O.combine_recv(comb, lay.send_pos, r["w"], T, k)
         got_out = bf16_np(B.out)
         check_combine_out(got_out, out)
+        check_combine_out(bf16_np(r["out_pull"]), out)     # the pulling combine gives the same bytes
 
 
 def check_combine_out(got: np.ndarray, ref: np.ndarray):

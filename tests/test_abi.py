@@ -11,7 +11,8 @@ import combine_lds_atomic_amd as moe
 
 def test_exports_every_declared_symbol():
     declared = moe.declared_symbols()
-    assert {"moe_dispatch_send", "moe_dispatch_recv", "moe_combine_send", "moe_combine_recv"} <= set(declared)
+    assert {"moe_dispatch_send", "moe_dispatch_recv", "moe_combine_send", "moe_combine_recv",
+            "moe_combine_pull"} <= set(declared)
     for name in declared:
         assert hasattr(moe.lib, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
@@ -78,6 +79,9 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     assert lib.moe_combine_send(s, _p(A + 2), _p(A), _p(A), _p(A), None) == -3
     assert lib.moe_combine_recv(s, _p(A), _p(A), None, _p(A), None) == -2
     assert lib.moe_combine_recv(s, _p(A), _p(A), _p(A), _p(A + 8), None) == -3
+    assert lib.moe_combine_pull(s, _p(A), _p(A), _p(A), _p(A), None, _p(A), None) == -2     # no ws
+    assert lib.moe_combine_pull(s, _p(A), None, _p(A), _p(A), _p(A), _p(A), None) == -2     # no ids
+    assert lib.moe_combine_pull(s, _p(A + 8), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -3
     fl = ctypes.c_uint32()
     assert lib.moe_status(None, None, ctypes.byref(fl)) == -2
     assert lib.moe_status(_p(A + 4), None, ctypes.byref(fl)) == -3

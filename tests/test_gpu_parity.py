@@ -198,6 +198,9 @@ def _sampled(r, lay, payload=True, n_tok=48, seed=0):
         got_out = bf16_np(B.out.reshape(N * T, H)[torch.from_numpy(toks).to(dev)])
         want = np.stack([O.combine_rows(ys[i], r["w"][s_[i], t_[i]]) for i in range(len(toks))])
         check_combine_out(got_out, want)
+        got_pull = bf16_np(r["out_pull"].reshape(N * T, H)[torch.from_numpy(toks).to(dev)])
+        check_combine_out(got_pull, want)
+        assert torch.equal(r["out_pull"].view(torch.int16), B.out.view(torch.int16)), "pull != send + recv"
 
 
 def _need(gib):
