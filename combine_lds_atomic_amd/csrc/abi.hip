@@ -82,6 +82,7 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->vprefix = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1)));
   W->exp_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.L + 1)));
   W->src_in_exp = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1) * D.E));
+  W->local = reinterpret_cast<int*>(take(D.B > 1 ? sizeof(int) * (size_t)D.N * D.TK : 0));
   return o;
 }
 

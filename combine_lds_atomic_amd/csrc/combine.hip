@@ -72,6 +72,10 @@ __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
 }
 
 constexpr int kSlotGroup = 8;
+#ifndef MOE_COMB_PIECES
+#define MOE_COMB_PIECES 2
+#endif
+constexpr int kCombPieces = MOE_COMB_PIECES;   // 1 KB pieces read per slot row per step
 
 // The weighted sum of one combine, token by token.  PULL = false: slot rows
 // are rank s's returned rows comb[s*T*k + send_pos].  PULL = true: they are
@@ -107,34 +111,52 @@ __device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const
       }
     }
     uint16_t* orow = out + (int64_t)tok * D.H;
-    for (int col = lane * 8; col < D.H; col += kWave * 8) {
-      float acc[8];
+    // Each step reads kCombPieces adjacent 1 KB pieces of every slot row
+    // (kCombPieces KB contiguous per row), lane l holding elements
+    // [base + c*512 + 8l, +8) of piece c.
+    for (int base = 0; base < D.H; base += kWave * 8 * kCombPieces) {
+      float acc[kCombPieces][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int c = 0; c < kCombPieces; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
       for (int j0 = 0; j0 < D.k; j0 += kSlotGroup) {
-        v4u v[kSlotGroup];
+        v4u v[kSlotGroup][kCombPieces];
         int rr[kSlotGroup];
 #pragma unroll
         for (int jj = 0; jj < kSlotGroup; ++jj) {
           const int j = j0 + jj;
           rr[jj] = j < D.k ? __builtin_amdgcn_readlane(row, j) : -1;
-          v[jj] = rr[jj] >= 0 ? ld16(reinterpret_cast<const v4u*>(rows + (int64_t)rr[jj] * D.H + col))
-                              : v4u{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < kCombPieces; ++c) {
+            const int col = base + c * kWave * 8 + lane * 8;
+            v[jj][c] = rr[jj] >= 0 && col < D.H
+                           ? ld16(reinterpret_cast<const v4u*>(rows + (int64_t)rr[jj] * D.H + col))
+                           : v4u{0, 0, 0, 0};
+          }
         }
 #pragma unroll
         for (int jj = 0; jj < kSlotGroup; ++jj) {
           const int j = j0 + jj;
           const float wj =
               __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), j < D.k ? j : 0));
-          if (rr[jj] >= 0) acc_row8(acc, wj, v[jj]);
+          if (rr[jj] >= 0) {
+#pragma unroll
+            for (int c = 0; c < kCombPieces; ++c) acc_row8(acc[c], wj, v[jj][c]);
+          }
         }
       }
-      v4u o;
-      o[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-      o[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-      o[2] = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-      o[3] = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-      st16(reinterpret_cast<v4u*>(orow + col), o);
+#pragma unroll
+      for (int c = 0; c < kCombPieces; ++c) {
+        const int col = base + c * kWave * 8 + lane * 8;
+        if (col >= D.H) continue;
+        v4u o;
+        o[0] = f32_to_bf16_rne(acc[c][0]) | (f32_to_bf16_rne(acc[c][1]) << 16);
+        o[1] = f32_to_bf16_rne(acc[c][2]) | (f32_to_bf16_rne(acc[c][3]) << 16);
+        o[2] = f32_to_bf16_rne(acc[c][4]) | (f32_to_bf16_rne(acc[c][5]) << 16);
+        o[3] = f32_to_bf16_rne(acc[c][6]) | (f32_to_bf16_rne(acc[c][7]) << 16);
+        st16(reinterpret_cast<v4u*>(orow + col), o);
+      }
     }
   }
 }

@@ -3,8 +3,9 @@
 // "Evaluation: dispatch/combine latency" for the block-scaled fp8 payload).
 //
 //   k_pack    each workgroup streams a contiguous range of tokens, one wave
-//             per token: final slot positions, block-128 amax with DPP, fp8
-//             quantisation, and k 16-byte row stores straight into the
+//             per token (or per slice of a token when tokens are too few to
+//             fill the GPU): final slot positions, block-128 amax with DPP,
+//             fp8 quantisation, and k 16-byte row stores straight into the
 //             destination ranks' receive regions (the "remote write").
 //   k_unpack  each workgroup streams a contiguous range of expert-major rows:
 //             the receive side finds each row's (expert, source) segment from
@@ -23,11 +24,6 @@
 #endif
 #ifndef MOE_PACK_PASSES
 #define MOE_PACK_PASSES 4
-#endif
-// Store order of the k copies: 0 = pass by pass (1 KB to each destination in
-// turn), 1 = the whole row to one destination, then the next.
-#ifndef MOE_PACK_ROW_STORES
-#define MOE_PACK_ROW_STORES 0
 #endif
 
 namespace moe {
@@ -53,14 +49,19 @@ __device__ __forceinline__ uint32_t quant4(const float* v, float scale) {
 #endif
 }
 
+// Work item = (token, slice): slice sl of a token covers passes
+// [sl*pps, (sl+1)*pps) of 1024 elements, pps = ceil(passes / slices).
 __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                      const int* __restrict__ idx, int* __restrict__ send_pos,
                                                      uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
   __shared__ float sscale[kPkWaves][kMaxNB];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int passes = (D.H + kPackCols - 1) / kPackCols;
+  const int pps = (passes + D.slices - 1) / D.slices;
   int lo, hi;
-  block_range(D.N * D.T, lo, hi);
-  for (int tok = lo + wv; tok < hi; tok += kPkWaves) {
+  block_range(D.N * D.T * D.slices, lo, hi);
+  for (int item = lo + wv; item < hi; item += kPkWaves) {
+    const int tok = item / D.slices, sl = item - tok * D.slices;
     const int s = tok / D.T, t = tok - s * D.T;
     // Lane j < k resolves slot j.  With one routing chunk per rank the count
     // kernel already wrote the final position; otherwise it left the rank
@@ -71,10 +72,12 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
       const int64_t slot = (int64_t)s * D.TK + i;
       const int e = idx[slot];
       if (e >= 0 && e < D.E) {
-        int sp = send_pos[slot];
+        int sp;
         if (D.B > 1) {
-          sp += W.blk[((int64_t)s * D.B + i / D.C) * D.E + e];
-          send_pos[slot] = sp;
+          sp = W.local[slot] + W.blk[((int64_t)s * D.B + i / D.C) * D.E + e];
+          if (sl == 0) send_pos[slot] = sp;
+        } else {
+          sp = send_pos[slot];
         }
         const int d = e / D.L;
         const int r = W.recv_off[d * (D.N + 1) + s] + sp - W.send_off[s * (D.E + 1) + d * D.L];
@@ -85,24 +88,22 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
     if (x == nullptr) continue;
 
     const uint16_t* xr = x + (int64_t)tok * D.H;
-    for (int c0 = 0; c0 < D.H; c0 += kPackCols * kPackPasses) {
+    const int h0 = sl * pps * kPackCols, h1 = min(D.H, (sl + 1) * pps * kPackCols);
+    for (int c0 = h0; c0 < h1; c0 += kPackCols * kPackPasses) {
       // Issue the loads of several passes before any math.
       v4u a[kPackPasses], b[kPackPasses];
-#if MOE_PACK_ROW_STORES
-      v4u qs[kPackPasses];
-#endif
 #pragma unroll
       for (int p = 0; p < kPackPasses; ++p) {
         const int col = c0 + p * kPackCols + lane * 16;
-        const bool act = col < D.H;
+        const bool act = col < h1;
         a[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col)) : v4u{0, 0, 0, 0};
         b[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col + 8)) : v4u{0, 0, 0, 0};
       }
 #pragma unroll
       for (int p = 0; p < kPackPasses; ++p) {
-        if (c0 + p * kPackCols >= D.H) break;
+        if (c0 + p * kPackCols >= h1) break;
         const int col = c0 + p * kPackCols + lane * 16;   // this lane's 16 elements
-        const bool act = col < D.H;                         // whole 8-lane groups drop out together
+        const bool act = col < h1;                          // whole 8-lane groups drop out together
         float v[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -123,30 +124,15 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
           for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
         }
         if (act && (lane & 7) == 0) sscale[wv][col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
-#if MOE_PACK_ROW_STORES
-        qs[p] = q;
-#else
         for (int j = 0; j < D.k; ++j) {
           const int rj = __builtin_amdgcn_readlane(row, j);
           if (rj >= 0 && act) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), q);
         }
-#endif
       }
-#if MOE_PACK_ROW_STORES
-      for (int j = 0; j < D.k; ++j) {
-        const int rj = __builtin_amdgcn_readlane(row, j);
-        if (rj < 0) continue;
-#pragma unroll
-        for (int p = 0; p < kPackPasses; ++p) {
-          const int col = c0 + p * kPackCols + lane * 16;
-          if (col < D.H) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), qs[p]);
-        }
-      }
-#endif
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    for (int bi = lane; bi < D.NB; bi += kWave) {
+    for (int bi = h0 / kScaleBlock + lane; bi < h1 / kScaleBlock; bi += kWave) {
       const float sc = sscale[wv][bi];
       for (int j = 0; j < D.k; ++j) {
         const int rj = __builtin_amdgcn_readlane(row, j);
@@ -218,10 +204,20 @@ __global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8
   }
 }
 
-int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
+int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
                 float* recv_s, int cus, hipStream_t st) {
-  if (D.N * D.T == 0) return MOE_OK;
-  const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T, kPkWaves);
+  if (D0.N * D0.T == 0) return MOE_OK;
+  // Split tokens into slices of their hidden dimension while there are fewer
+  // tokens than the GPU holds waves (about 32 per CU), so small batches still
+  // keep enough loads and stores in flight.
+  Dims D = D0;
+  const int64_t tokens = (int64_t)D.N * D.T;
+  const int passes = (D.H + kPackCols - 1) / kPackCols;
+  const int64_t wave_slots = (int64_t)cus * 32;
+  D.slices = 1;
+  if (x != nullptr)
+    while (D.slices * 2 <= passes && tokens * D.slices * 2 <= wave_slots) D.slices *= 2;
+  const int grid = stream_grid(kPackShape, cus, tokens * D.slices, kPkWaves);
   return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
 }
 

@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kThreads) void k_route_count(Dims D, Ws W, const in
   for (int bt = 0; bt < kMaxBatches; ++bt) {
     if (bt * kWave >= per_wave) break;
     const int i = c0 + bt * kWave + lane;
-    if (i < cend) send_pos[rbase + i] = ev[bt] >= 0 ? wr[ev[bt]] + rv[bt] : -1;
+    if (i >= cend) continue;
+    const int v = ev[bt] >= 0 ? wr[ev[bt]] + rv[bt] : -1;
+    if (D.B == 1) send_pos[rbase + i] = v;   // final position
+    else W.local[rbase + i] = v;             // rank inside the chunk; the pack adds the chunk base
   }
 }
 

@@ -57,6 +57,7 @@ struct Dims {
   int C;        // routing chunk, slots
   int B;        // routing chunks per rank
   int NB;       // scale blocks per row = H/128
+  int slices;   // pack work items per token (1 = whole row per wave)
   int R;        // fixed region rows, 0 = packed
   int rows;     // rows of every receive / expert-major array
   int64_t bound;  // N*T*max(k, L)
@@ -74,6 +75,7 @@ struct Ws {
   int *vprefix;       // [N+1] running total of rows written per region
   int *exp_off;       // [N][L+1]
   int *src_in_exp;    // [N+1][E] rows of expert e from sources before s
+  int *local;         // [N][T*k] rank of each slot inside its chunk (several chunks per rank)
 };
 
 // ------------------------------------------------------------------ helpers
@@ -155,7 +157,7 @@ struct LaunchShape {
 #define MOE_COMB_SEND_SHAPE {16, 1}
 #endif
 #ifndef MOE_COMB_RECV_SHAPE
-#define MOE_COMB_RECV_SHAPE {4, 4}
+#define MOE_COMB_RECV_SHAPE {4, 8}
 #endif
 constexpr LaunchShape kPackShape = MOE_PACK_SHAPE;
 constexpr LaunchShape kUnpackShape = MOE_UNPACK_SHAPE;
