@@ -180,6 +180,26 @@ def main():
     nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k, Tc)
     total = sum(nbytes[p] for p in PHASES)
 
+    # The same step captured once in a HIP graph and replayed (no launch gaps).
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        step()
+    stream.wait_stream(cap)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_step_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(2):
@@ -250,6 +270,7 @@ def main():
         "combine_frac": round((nbytes["combine_send"] + nbytes["combine_recv"]) /
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
+        "graph_step_us": round(graph_step_ms * 1e3, 1),
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
