@@ -11,7 +11,9 @@ dispatch batch and the combine on the layout of an untimed, payload-free
 dispatch at the combine batch.
 
 The pulling combine (moe_combine_pull) is timed after the steps, on the same
-data, and reported beside them; it is not part of the step.
+data, and reported beside them; it is not part of the step.  So is, when every
+rank's slots fit one routing chunk (T*k <= 4096), the step with the
+single-launch moe_dispatch_send_ll in place of moe_dispatch_send.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -147,9 +149,9 @@ def main():
     y = W.expert_outputs(cfg, Bc.rows, dev)
     out_pull = torch.empty_like(Bc.out)
 
-    def step(ev=None):
+    def step(ev=None, send=moe.moe_dispatch_send):
         if ev: ev[0].record(stream)
-        moe.moe_dispatch_send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
+        send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
         if ev: ev[1].record(stream)
         moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
         if ev: ev[2].record(stream)
@@ -181,24 +183,53 @@ def main():
     total = sum(nbytes[p] for p in PHASES)
 
     # The same step captured once in a HIP graph and replayed (no launch gaps).
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        step()
-    stream.wait_stream(cap)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    graph.replay()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
+    def graph_ms(send):
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step(send=send)
+        stream.wait_stream(cap)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(send=send)
+        torch.cuda.synchronize()
         graph.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_step_ms = g0.elapsed_time(g1) / args.steps
-    del graph
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return g0.elapsed_time(g1) / args.steps
+
+    graph_step_ms = graph_ms(moe.moe_dispatch_send)
+
+    # The single-launch dispatch (moe_dispatch_send_ll, one routing chunk per
+    # rank only) in the same step in place of moe_dispatch_send: its phase
+    # time, the eager and graph-replayed step, and a bitwise comparison of its
+    # outputs with the multi-launch call's.
+    single = None
+    if T * cfg.k <= 4096 and T > 0:
+        ref = {f: getattr(B, f).clone() for f in ("send_pos", "recv_q", "recv_s", "x_q", "x_s", "row_src")}
+        for _ in range(args.warmup):
+            step(send=moe.moe_dispatch_send_ll)
+        evl = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evl[i], send=moe.moe_dispatch_send_ll)
+        torch.cuda.synchronize()
+        wall_l = time.perf_counter() - t0
+        same = all(torch.equal(getattr(B, f).view(torch.uint8) if ref[f].dtype != torch.int32 else getattr(B, f),
+                               ref[f].view(torch.uint8) if ref[f].dtype != torch.int32 else ref[f]) for f in ref)
+        ms_l = np.array([[evl[i][p].elapsed_time(evl[i][p + 1]) for p in range(4)] for i in range(args.steps)])
+        single = {"call": "moe_dispatch_send_ll", "dispatch_send": None,
+                  "step_us": round(wall_l * 1e6 / args.steps, 1),
+                  "graph_step_us": round(graph_ms(moe.moe_dispatch_send_ll) * 1e3, 1),
+                  "same_bytes_as_dispatch_send": bool(same)}
+        single_ms = ms_l.mean(axis=0)[0]
+        single_p90 = np.percentile(ms_l[:, 0], 90)
 
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -241,6 +272,8 @@ def main():
         return d
 
     phase_info = {name: info(name, per_phase_ms[p], p90_ms[p]) for p, name in enumerate(PHASES)}
+    if single is not None:
+        single["dispatch_send"] = info("dispatch_send", single_ms, single_p90)
     dom_name = PHASES[dom]
     achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
     kernel = KERNEL_OF[dom_name]
@@ -271,6 +304,7 @@ def main():
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
         "graph_step_us": round(graph_step_ms * 1e3, 1),
+        "single_launch_dispatch": single,
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe_ep.h")
 
 MOE_OK = 0
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_ENULL", -3: "MOE_EALIGN", -4: "MOE_ERANGE", -5: "MOE_EHIP"}
-FLAG_BADID, FLAG_OVERFLOW, FLAG_BOUND = 1, 2, 4
+FLAG_BADID, FLAG_OVERFLOW, FLAG_BOUND, FLAG_TIMEOUT = 1, 2, 4, 8
 
 
 class MoeError(RuntimeError):
@@ -71,6 +71,7 @@ _SIG = {
     "moe_workspace_bytes": (ctypes.c_int64, [_S]),
     "moe_workspace_init": (ctypes.c_int, [_S, _P, _P]),
     "moe_dispatch_send": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_send_ll": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine_send": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "moe_combine_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
@@ -129,6 +130,12 @@ def moe_workspace_init(sh, ws, stream=None):
 def moe_dispatch_send(sh, tokens, topk_idx, recv_q, recv_s, send_pos, ws, stream=None):
     _check("moe_dispatch_send", lib.moe_dispatch_send(ctypes.byref(sh), _ptr(tokens), _ptr(topk_idx), _ptr(recv_q),
                                                       _ptr(recv_s), _ptr(send_pos), _ptr(ws), _stream(stream)))
+
+
+def moe_dispatch_send_ll(sh, tokens, topk_idx, recv_q, recv_s, send_pos, ws, stream=None):
+    _check("moe_dispatch_send_ll", lib.moe_dispatch_send_ll(ctypes.byref(sh), _ptr(tokens), _ptr(topk_idx),
+                                                            _ptr(recv_q), _ptr(recv_s), _ptr(send_pos), _ptr(ws),
+                                                            _stream(stream)))
 
 
 def moe_dispatch_recv(sh, recv_q, recv_s, ws, x_q, x_s, exp_off, row_src, stream=None):

@@ -83,8 +83,20 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->exp_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.L + 1)));
   W->src_in_exp = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1) * D.E));
   W->local = reinterpret_cast<int*>(take(D.B > 1 ? sizeof(int) * (size_t)D.N * D.TK : 0));
+  // Exchange area of the single-launch dispatch (one routing chunk per rank
+  // only), last so that moe_workspace_init clears it with the header.
+  const bool ll = D.B == 1;
+  auto take64 = [&](size_t n) { return reinterpret_cast<uint64_t*>(take(ll ? sizeof(uint64_t) * n : 0)); };
+  W->ctl = reinterpret_cast<uint32_t*>(take(ll ? sizeof(uint32_t) * (kCtlGroups + 1) * kCtlStride : 0));
+  W->tpos = take64((size_t)D.N * D.TK);
+  W->toff = take64((size_t)D.N * (D.N + 1));
+  W->tcnt = take64((size_t)D.N * D.E);
+  W->trel = take64((size_t)D.N * D.N);
+  W->tbase = take64((size_t)D.N);
+  W->tready = take64((size_t)kReadyCopies * kReadyStride);
   return o;
 }
+
 
 // Compute units of the current device, cached per device.
 int device_cus() {
@@ -136,7 +148,13 @@ int moe_workspace_init(const moe_shape* shape, void* ws, void* stream) {
   if (rc) return rc;
   if (!ws) return MOE_ENULL;
   if (!aligned(ws, kAlign)) return MOE_EALIGN;
-  return launch_fill_u32(static_cast<uint32_t*>(ws), 0u, (int)(kAlign / sizeof(uint32_t)), as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  rc = launch_fill_u32(static_cast<uint32_t*>(ws), 0u, (int)(kAlign / sizeof(uint32_t)), st);
+  if (rc || D.B != 1) return rc;
+  Ws W;
+  const size_t total = carve(D, ws, &W);
+  const size_t x0 = static_cast<size_t>(reinterpret_cast<char*>(W.ctl) - static_cast<char*>(ws));
+  return launch_fill_u32(W.ctl, 0u, (int)((total - x0) / sizeof(uint32_t)), st);
 }
 
 int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* recv_q,
@@ -157,6 +175,23 @@ int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int3
   rc = launch_route(D, W, topk_idx, send_pos, st);
   if (rc) return rc;
   return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s, device_cus(), st);
+}
+
+int moe_dispatch_send_ll(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* recv_q,
+                         float* recv_s, int32_t* send_pos, void* ws, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  if (D.T == 0) return launch_route(D, W_of(D, ws), topk_idx, send_pos, as_stream(stream));   // nothing to exchange
+  if (D.B != 1) return MOE_EINVAL;   // more than one routing chunk per rank
+  if (!topk_idx || !send_pos) return MOE_ENULL;
+  if (tokens && (!recv_q || !recv_s)) return MOE_ENULL;
+  if (!aligned(topk_idx, 4) || !aligned(send_pos, 4)) return MOE_EALIGN;
+  if (tokens && (!aligned(tokens, 16) || !aligned(recv_q, 16) || !aligned(recv_s, 4))) return MOE_EALIGN;
+  return launch_dispatch_ll(D, W_of(D, ws), tokens, topk_idx, send_pos, recv_q, recv_s, device_cus(),
+                            as_stream(stream));
 }
 
 int moe_dispatch_recv(const moe_shape* shape, const uint8_t* recv_q, const float* recv_s, const void* ws,

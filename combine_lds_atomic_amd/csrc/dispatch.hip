@@ -11,7 +11,10 @@
 //             the receive side finds each row's (expert, source) segment from
 //             the exchanged counts alone and copies it out of the
 //             source-major receive region.
-#include "moe_internal.h"
+#include <map>
+#include <mutex>
+
+#include "route_dev.h"
 
 // fp32 -> e4m3fn conversion.  Both variants give the same bytes on the
 // whole input domain (every bfloat16 pair x <= amax), which the exhaustive
@@ -49,19 +52,120 @@ __device__ __forceinline__ uint32_t quant4(const float* v, float scale) {
 #endif
 }
 
-// Work item = (token, slice): slice sl of a token covers passes
-// [sl*pps, (sl+1)*pps) of 1024 elements, pps = ceil(passes / slices).
+// This lane's 16 elements of each pass of the chunk starting at column c0
+// (zero beyond h1).
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ xr, int c0, int h1, int lane,
+                                           v4u (&a)[kPackPasses], v4u (&b)[kPackPasses]) {
+#pragma unroll
+  for (int p = 0; p < kPackPasses; ++p) {
+    const int col = c0 + p * kPackCols + lane * 16;
+    const bool act = col < h1;
+    a[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col)) : v4u{0, 0, 0, 0};
+    b[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col + 8)) : v4u{0, 0, 0, 0};
+  }
+}
+
+// One pass of a pack work item: this lane's 16 elements at column col (all
+// in one 128-element block shared with 7 neighbouring lanes): block amax,
+// scale, fp8 bytes, the k row stores; the scale goes to the wave's LDS row.
+__device__ __forceinline__ void pack_pass(const Dims& D, const v4u& a, const v4u& b, int col, bool act, int row,
+                                          int lane, uint8_t* __restrict__ recv_q, float* ssw) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(a[i]);
+    v[2 * i + 1] = bf16_hi(a[i]);
+    v[8 + 2 * i] = bf16_lo(b[i]);
+    v[8 + 2 * i + 1] = bf16_hi(b[i]);
+  }
+  int am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
+  am = max8_lanes(am);                     // amax of the 128-element block
+  const float amax = __uint_as_float((uint32_t)am);
+  const float scale = amax / 448.0f;       // IEEE division, round to nearest even
+  v4u q = {0, 0, 0, 0};
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
+  }
+  if (act && (lane & 7) == 0) ssw[col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
+  for (int j = 0; j < D.k; ++j) {
+    const int rj = __builtin_amdgcn_readlane(row, j);
+    if (rj >= 0 && act) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), q);
+  }
+}
+
+// The scales of columns [h0, h1) from the wave's LDS row to the k rows.
+__device__ __forceinline__ void pack_scales(const Dims& D, int h0, int h1, int row, int lane,
+                                            float* __restrict__ recv_s, const float* ssw) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int bi = h0 / kScaleBlock + lane; bi < h1 / kScaleBlock; bi += kWave) {
+    const float sc = ssw[bi];
+    for (int j = 0; j < D.k; ++j) {
+      const int rj = __builtin_amdgcn_readlane(row, j);
+      if (rj >= 0) recv_s[(int64_t)rj * D.NB + bi] = sc;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Work item = (token, slice): slice sl of a token covers columns [h0, h1),
+// passes [sl*pps, (sl+1)*pps) of 1024 elements, pps = ceil(passes / slices).
+__device__ __forceinline__ void item_cols(const Dims& D, int item, int& tok, int& sl, int& h0, int& h1) {
+  const int passes = (D.H + kPackCols - 1) / kPackCols;
+  const int pps = (passes + D.slices - 1) / D.slices;
+  tok = item / D.slices;
+  sl = item - tok * D.slices;
+  h0 = sl * pps * kPackCols;
+  h1 = min(D.H, (sl + 1) * pps * kPackCols);
+}
+
+// Pack work item `item` with the calling wave, whose rows are already
+// resolved (lane j < k: receive row of slot j, -1 for none).  LOADED: pa and
+// pb hold the item's first chunk.
+template <bool LOADED>
+__device__ __forceinline__ void pack_item(const Dims& D, int item, int row, const uint16_t* __restrict__ x,
+                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s, float* ssw,
+                                          const v4u* pa = nullptr, const v4u* pb = nullptr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int tok, sl, h0, h1;
+  item_cols(D, item, tok, sl, h0, h1);
+  const uint16_t* xr = x + (int64_t)tok * D.H;
+  int c0 = h0;
+  if (LOADED) {   // the first chunk, peeled so its registers die here
+#pragma unroll
+    for (int p = 0; p < kPackPasses; ++p) {
+      if (c0 + p * kPackCols >= h1) break;
+      const int col = c0 + p * kPackCols + lane * 16;
+      pack_pass(D, pa[p], pb[p], col, col < h1, row, lane, recv_q, ssw);
+    }
+    c0 += kPackCols * kPackPasses;
+  }
+  for (; c0 < h1; c0 += kPackCols * kPackPasses) {
+    v4u a[kPackPasses], b[kPackPasses];
+    load_chunk(xr, c0, h1, lane, a, b);   // the loads of several passes before any math
+#pragma unroll
+    for (int p = 0; p < kPackPasses; ++p) {
+      if (c0 + p * kPackCols >= h1) break;
+      const int col = c0 + p * kPackCols + lane * 16;   // this lane's 16 elements
+      pack_pass(D, a[p], b[p], col, col < h1, row, lane, recv_q, ssw);   // whole 8-lane groups drop out together
+    }
+  }
+  pack_scales(D, h0, h1, row, lane, recv_s, ssw);
+}
+
 __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                      const int* __restrict__ idx, int* __restrict__ send_pos,
                                                      uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
   __shared__ float sscale[kPkWaves][kMaxNB];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int passes = (D.H + kPackCols - 1) / kPackCols;
-  const int pps = (passes + D.slices - 1) / D.slices;
   int lo, hi;
   block_range(D.N * D.T * D.slices, lo, hi);
   for (int item = lo + wv; item < hi; item += kPkWaves) {
-    const int tok = item / D.slices, sl = item - tok * D.slices;
+    int tok, sl, h0, h1;
+    item_cols(D, item, tok, sl, h0, h1);
     const int s = tok / D.T, t = tok - s * D.T;
     // Lane j < k resolves slot j.  With one routing chunk per rank the count
     // kernel already wrote the final position; otherwise it left the rank
@@ -86,60 +190,333 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
       }
     }
     if (x == nullptr) continue;
+    pack_item<false>(D, item, row, x, recv_q, recv_s, sscale[wv]);
+  }
+}
 
-    const uint16_t* xr = x + (int64_t)tok * D.H;
-    const int h0 = sl * pps * kPackCols, h1 = min(D.H, (sl + 1) * pps * kPackCols);
-    for (int c0 = h0; c0 < h1; c0 += kPackCols * kPackPasses) {
-      // Issue the loads of several passes before any math.
-      v4u a[kPackPasses], b[kPackPasses];
+// ------------------------------------------------------------------ single launch
+//
+// The whole send half of dispatch in one launch, without a host round trip
+// or a kernel boundary between the count exchange and the payload stores
+// (AWS China blog "750B MoE model migration from a self-built RoCE cluster to
+// AWS EFA", section 4.4, "DeepEP low-latency mode": one kernel per dispatch,
+// no CPU in the loop, capturable in a graph).  The workgroup index gives
+// the role:
+//   b <  N   count rank b's slots (count_chunk) and publish them;
+//   b == N   the cross-rank scans: receive offsets and region bases for the
+//            packers first, then the tables dispatch_recv reads;
+//   b >  N   pack: load tokens while the layout is being computed, then
+//            quantise and store the rows once the positions are known.
+// A workgroup only ever waits for values that workgroups with smaller
+// indices produce.  The dispatcher hands each XCD its workgroups in index
+// order, so the N + 1 layout workgroups are the first on their XCDs and are
+// resident before any packer that could wait for them.  Every wait is also
+// bounded (kSpinLimit): were that order ever not kept, a wait would end with
+// MOE_FLAG_TIMEOUT instead of hanging.  (Taking a ticket from one global
+// counter would not need the order, but its one atomic per workgroup on a
+// single address serialises: about 8 ns each, 15 us for a decode-sized
+// grid.)
+//
+// Signalling departs from the fence-then-signal pattern of the Perseus
+// write-up (section 3.2, decoupled signaling: one fence per group of puts,
+// then the group's signals): on a multi-XCD MI355X a release fence writes
+// back the whole L2 of the XCD, so instead every exchanged value carries the
+// call's tag in the same 8-byte atomic store and is its own completion
+// signal; no fence is issued at all.  The packers poll one of kReadyCopies
+// replicated "ready" words, published after the values they need, then read
+// their values (normally already there, otherwise they keep polling those).
+
+// v[u] = value of p[u * stride] for u < n (n <= M), once all carry `tag`;
+// false after kSpinLimit polls.
+template <int M>
+__device__ __forceinline__ bool tag_wait_n(const uint64_t* p, int64_t stride, int n, uint32_t tag, int (&v)[M]) {
+  uint64_t u[M];
 #pragma unroll
-      for (int p = 0; p < kPackPasses; ++p) {
-        const int col = c0 + p * kPackCols + lane * 16;
-        const bool act = col < h1;
-        a[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col)) : v4u{0, 0, 0, 0};
-        b[p] = act ? ld16(reinterpret_cast<const v4u*>(xr + col + 8)) : v4u{0, 0, 0, 0};
-      }
+  for (int i = 0; i < M; ++i) u[i] = i < n ? tag_load(p + i * stride) : ((uint64_t)tag << 32);
+  for (int it = 0;; ++it) {
+    bool ok = true;
 #pragma unroll
-      for (int p = 0; p < kPackPasses; ++p) {
-        if (c0 + p * kPackCols >= h1) break;
-        const int col = c0 + p * kPackCols + lane * 16;   // this lane's 16 elements
-        const bool act = col < h1;                          // whole 8-lane groups drop out together
-        float v[16];
+    for (int i = 0; i < M; ++i) ok = ok && tag_ok(u[i], tag);
+    if (ok) break;
+    if (it == kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_lo(a[p][i]);
-          v[2 * i + 1] = bf16_hi(a[p][i]);
-          v[8 + 2 * i] = bf16_lo(b[p][i]);
-          v[8 + 2 * i + 1] = bf16_hi(b[p][i]);
-        }
-        int am = 0;
+    for (int i = 0; i < M; ++i)
+      if (!tag_ok(u[i], tag)) u[i] = tag_load(p + i * stride);
+  }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
-        am = max8_lanes(am);                     // amax of the 128-element block
-        const float amax = __uint_as_float((uint32_t)am);
-        const float scale = amax / 448.0f;       // IEEE division, round to nearest even
-        v4u q = {0, 0, 0, 0};
-        if (amax != 0.0f) {
+  for (int i = 0; i < M; ++i) v[i] = (int)(uint32_t)u[i];
+  return true;
+}
+
+// Three tagged values at once (p2 may be NULL: v2 is left as it is).
+__device__ __forceinline__ bool tag_wait3(const uint64_t* p0, const uint64_t* p1, const uint64_t* p2, uint32_t tag,
+                                          int& v0, int& v1, int& v2) {
+  const uint64_t ok2 = (uint64_t)tag << 32;
+  uint64_t u0 = tag_load(p0), u1 = tag_load(p1), u2 = p2 ? tag_load(p2) : ok2;
+  for (int it = 0; !(tag_ok(u0, tag) && tag_ok(u1, tag) && tag_ok(u2, tag)); ++it) {
+    if (it == kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(2);
+    if (!tag_ok(u0, tag)) u0 = tag_load(p0);
+    if (!tag_ok(u1, tag)) u1 = tag_load(p1);
+    if (!tag_ok(u2, tag)) u2 = tag_load(p2);
+  }
+  v0 = (int)(uint32_t)u0;
+  v1 = (int)(uint32_t)u1;
+  if (p2) v2 = (int)(uint32_t)u2;
+  return true;
+}
+
+// Tagged values the cross-rank role polls at once per thread (register
+// budget: every role of the launch shares the pack role's 64 VGPRs).
+constexpr int kCrossBatch = 4;
+
+// LDS bytes of the cross-rank role.
+inline size_t cross_ll_lds_bytes(int E) { return sizeof(int) * ((size_t)kThreads + E + 1); }
+
+// The cross-rank role: the same tables k_route_cross computes, from the
+// tagged send offsets and counts of the count workgroups.
+__device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int* wsum) {
+  const int N = D.N, E = D.E, L = D.L, tid = threadIdx.x;
+  int* part = sm;              // [G][N], G*N <= kThreads
+  int* ex = sm + kThreads;     // [E+1]
+  bool ok = true;
+
+  // (1) rows from source s to destination d are
+  // send_off[s][(d+1)L] - send_off[s][dL]; thread (g, d) sums them over its
+  // share of the sources.
+  const int G = max(1, kThreads / N);
+  const int d = tid % N, g = tid / N;
+  const bool mine = g < G;
+  const int per = (N + G - 1) / G;
+  const int s0 = min(N, g * per), s1 = min(N, s0 + per);
+  const int64_t ld = N + 1;
+  // A thread whose sources fit one batch keeps the values for step (3).
+  int lo1[kCrossBatch] = {}, hi1[kCrossBatch] = {};
+  const bool one = s1 - s0 <= kCrossBatch;
+  if (mine) {
+    int sum = 0;
+    for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
+      const int n = min(kCrossBatch, s1 - sb);
+      int lo[kCrossBatch] = {}, hi[kCrossBatch] = {};
+      ok = tag_wait_n(W.toff + sb * ld + d, ld, n, tag, lo) && tag_wait_n(W.toff + sb * ld + d + 1, ld, n, tag, hi);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
-        }
-        if (act && (lane & 7) == 0) sscale[wv][col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
-        for (int j = 0; j < D.k; ++j) {
-          const int rj = __builtin_amdgcn_readlane(row, j);
-          if (rj >= 0 && act) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), q);
-        }
+      for (int u = 0; u < kCrossBatch; ++u) {
+        sum += hi[u] - lo[u];
+        lo1[u] = lo[u];
+        hi1[u] = hi[u];
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    for (int bi = h0 / kScaleBlock + lane; bi < h1 / kScaleBlock; bi += kWave) {
-      const float sc = sscale[wv][bi];
-      for (int j = 0; j < D.k; ++j) {
-        const int rj = __builtin_amdgcn_readlane(row, j);
-        if (rj >= 0) recv_s[(int64_t)rj * D.NB + bi] = sc;
+    part[g * N + d] = sum;
+  }
+  __syncthreads();
+  int rt = 0;   // rows received by rank tid
+  if (tid < N) {
+    int a = 0;
+    for (int g2 = 0; g2 < G; ++g2) {
+      const int c = part[g2 * N + tid];
+      part[g2 * N + tid] = a;
+      a += c;
+    }
+    rt = a;
+  }
+  // (2) Region bases, rows written per region, capacity and bound checks.
+  int all, vall;
+  const int b = block_scan<kThreads>(rt, wsum, &all);
+  const int vb = block_scan<kThreads>(D.R ? min(rt, D.R) : rt, wsum, &vall);
+  if (tid < N) {
+    const int bd = D.R ? tid * D.R : b;
+    tag_put(W.tbase + tid, tag, bd);
+    W.base[tid] = bd;
+    W.vprefix[tid] = vb;
+    W.recv_total[tid] = rt;
+    W.recv_off[tid * (N + 1) + N] = rt;
+    uint32_t fl = 0;
+    if (D.R && rt > D.R) fl |= MOE_FLAG_OVERFLOW;
+    if ((int64_t)rt > D.bound) fl |= MOE_FLAG_BOUND;
+    if (fl) atomicOr(W.err, fl);
+  }
+  if (tid == 0) {
+    W.base[N] = D.R ? N * D.R : all;
+    W.vprefix[N] = vall;
+  }
+  // (3) recv_off[d][s], and what a packer of source s adds to a sender
+  // position to get its row inside region d: recv_off[d][s] - send_off[s][dL].
+  if (mine && ok) {
+    int acc = part[g * N + d];
+    for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
+      const int n = min(kCrossBatch, s1 - sb);
+      int lo[kCrossBatch], hi[kCrossBatch];
+#pragma unroll
+      for (int u = 0; u < kCrossBatch; ++u) {
+        lo[u] = lo1[u];
+        hi[u] = hi1[u];
+      }
+      if (!one)
+        ok = tag_wait_n(W.toff + sb * ld + d, ld, n, tag, lo) && tag_wait_n(W.toff + sb * ld + d + 1, ld, n, tag, hi);
+      for (int u = 0; u < n && ok; ++u) {
+        const int s = sb + u;
+        W.recv_off[d * (N + 1) + s] = acc;
+        tag_put(W.trel + (int64_t)s * N + d, tag, acc - lo[u]);
+        acc += hi[u] - lo[u];
       }
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  if (tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
+
+  // (4) Off the packers' path: src_in_exp and exp_off for dispatch_recv.
+  for (int e = tid; e < E; e += kThreads) {
+    int acc = 0;
+    for (int sb = 0; sb < N && ok; sb += kCrossBatch) {
+      const int n = min(kCrossBatch, N - sb);
+      int c[kCrossBatch] = {};
+      ok = tag_wait_n(W.tcnt + (int64_t)sb * E + e, E, n, tag, c);
+      for (int u = 0; u < n && ok; ++u) {
+        W.src_in_exp[(sb + u) * E + e] = acc;
+        acc += c[u];
+      }
+    }
+    W.src_in_exp[N * E + e] = acc;
+    ex[e] = acc;
+  }
+  __syncthreads();
+  {
+    // Exclusive scan over all experts, four per thread (E <= 1024).
+    const int e0 = min(E, tid * 4), e1 = min(E, e0 + 4);
+    int v = 0;
+    for (int e = e0; e < e1; ++e) v += ex[e];
+    int etot;
+    int x = block_scan<kThreads>(v, wsum, &etot);
+    for (int e = e0; e < e1; ++e) {
+      const int c = ex[e];
+      ex[e] = x;
+      x += c;
+    }
+    if (tid == 0) ex[E] = etot;
+  }
+  __syncthreads();
+  for (int i = tid; i < N * (L + 1); i += kThreads) {
+    const int dd = i / (L + 1), l = i - dd * (L + 1);
+    W.exp_off[i] = ex[dd * L + l] - ex[dd * L];
+  }
+  if (!ok) atomicOr(W.err, MOE_FLAG_TIMEOUT);
+}
+
+static_assert(kPkThreads == kThreads, "the single-launch dispatch runs every role with 256 threads");
+
+// LDS bytes of the pack role (per-wave scales of one token row).
+inline size_t pack_lds_bytes(int NB) { return sizeof(float) * (size_t)kPkWaves * NB; }
+
+__global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                          const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
+                                                          int npack) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int wsum[kWavesPerBlock + 1];
+  __shared__ int sh_fail;
+  __shared__ uint32_t sh_epoch;
+  const int wg = blockIdx.x;
+  const int grp = wg % kCtlGroups;
+  uint32_t* gline = W.ctl + grp * kCtlStride;   // [0] finished workgroups, [1] call number
+  if (threadIdx.x == 0) {
+    sh_epoch = __hip_atomic_load(gline + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_fail = 0;
+  }
+  __syncthreads();
+  const uint32_t tag = epoch_tag(sh_epoch);
+
+  if (wg < D.N) {
+    count_chunk(D, W, idx, send_pos, wg, 0, smem, wsum, tag);
+  } else if (wg == D.N) {
+    cross_ll(D, W, tag, reinterpret_cast<int*>(smem), wsum);
+  } else {
+    const int p = wg - D.N - 1;
+    const int items = D.N * D.T * D.slices;
+    const int lo = (int)((int64_t)items * p / npack), hi = (int)((int64_t)items * (p + 1) / npack);
+    bool fail = false;
+    auto gate = [&] {
+      if (threadIdx.x == 0) {
+        int one;
+        if (!tag_wait(W.tready + (p % kReadyCopies) * kReadyStride, tag, &one)) {
+          sh_fail = 1;
+          atomicOr(W.err, MOE_FLAG_TIMEOUT);
+        }
+      }
+      __syncthreads();
+      fail = sh_fail != 0;
+    };
+    // Expert of slot j (lane j < k) of work item `item`.
+    auto expert = [&](int item) {
+      const int lane = threadIdx.x & (kWave - 1);
+      const int tok = item / D.slices;
+      return lane < D.k ? idx[(int64_t)tok * D.k + lane] : -1;
+    };
+    // Rows of slot j (lane j < k) of work item `item`, expert e, from the
+    // tagged positions and offsets.
+    auto resolve = [&](int item, int e) {
+      const int lane = threadIdx.x & (kWave - 1);
+      const int tok = item / D.slices;
+      const int s = tok / D.T;
+      int row = -1;
+      bool ok = true;
+      if (!fail && lane < D.k) {
+        const int64_t slot = (int64_t)tok * D.k + lane;
+        if (e >= 0 && e < D.E) {
+          const int d = e / D.L;
+          int sp = 0, rel = 0, bd = D.R ? d * D.R : 0;
+          ok = tag_wait3(W.tpos + slot, W.trel + (int64_t)s * D.N + d, D.R ? nullptr : W.tbase + d, tag, sp, rel, bd);
+          const int r = rel + sp;
+          const int pr = bd + r;
+          if (ok && (D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
+        }
+      }
+      if (__any(!ok)) {   // stop waiting for anything else in this wave
+        fail = true;
+        if (lane == 0) atomicOr(W.err, MOE_FLAG_TIMEOUT);
+      }
+      return row;
+    };
+    // Each wave loads its first item's first chunk, then the workgroup waits
+    // for the layout, then packs.
+    const int wv = threadIdx.x / kWave;
+    float* ssw = reinterpret_cast<float*>(smem) + wv * D.NB;
+    int item = lo + wv;
+    const bool has = item < hi;
+    v4u a[kPackPasses], b[kPackPasses];
+    int e1 = -1;
+    if (has) {
+      int tok, sl, h0, h1;
+      item_cols(D, item, tok, sl, h0, h1);
+      load_chunk(x + (int64_t)tok * D.H, h0, h1, threadIdx.x & (kWave - 1), a, b);
+      e1 = expert(item);
+    }
+    gate();
+    if (has) {
+      pack_item<true>(D, item, resolve(item, e1), x, recv_q, recv_s, ssw, a, b);
+      item += kPkWaves;
+    }
+    for (; item < hi; item += kPkWaves) pack_item<false>(D, item, resolve(item, expert(item)), x, recv_q, recv_s, ssw);
+  }
+
+  // The last workgroup of each group to finish clears the group's counter and
+  // counts the group as done; the last group to finish advances every
+  // group's call number for the next launch on this workspace (all
+  // workgroups of this launch have read theirs by then).
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int G = gridDim.x;
+    const uint32_t members = (uint32_t)((G - grp + kCtlGroups - 1) / kCtlGroups);
+    const uint32_t groups = (uint32_t)min(G, kCtlGroups);
+    if (__hip_atomic_fetch_add(gline, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+      __hip_atomic_store(gline, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t* all = W.ctl + kCtlGroups * kCtlStride;
+      if (__hip_atomic_fetch_add(all, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1) {
+        __hip_atomic_store(all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < kCtlGroups; ++g)
+          __hip_atomic_store(W.ctl + g * kCtlStride + 1, sh_epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -204,20 +581,25 @@ __global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8
   }
 }
 
-int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
-                float* recv_s, int cus, hipStream_t st) {
-  if (D0.N * D0.T == 0) return MOE_OK;
-  // Split tokens into slices of their hidden dimension while there are fewer
-  // tokens than the GPU holds waves (about 32 per CU), so small batches still
-  // keep enough loads and stores in flight.
-  Dims D = D0;
+// Slices of its hidden dimension each token is split into: doubled while
+// there are fewer work items than the GPU holds waves (about 32 per CU), so
+// small batches still keep enough loads and stores in flight.
+static int pack_slices(const Dims& D, int cus, bool payload) {
   const int64_t tokens = (int64_t)D.N * D.T;
   const int passes = (D.H + kPackCols - 1) / kPackCols;
   const int64_t wave_slots = (int64_t)cus * 32;
-  D.slices = 1;
-  if (x != nullptr)
-    while (D.slices * 2 <= passes && tokens * D.slices * 2 <= wave_slots) D.slices *= 2;
-  const int grid = stream_grid(kPackShape, cus, tokens * D.slices, kPkWaves);
+  int sl = 1;
+  if (payload)
+    while (sl * 2 <= passes && tokens * sl * 2 <= wave_slots) sl *= 2;
+  return sl;
+}
+
+int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
+                float* recv_s, int cus, hipStream_t st) {
+  if (D0.N * D0.T == 0) return MOE_OK;
+  Dims D = D0;
+  D.slices = pack_slices(D, cus, x != nullptr);
+  const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
   return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
 }
 
@@ -226,6 +608,52 @@ int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float
   const int grid = stream_grid(kUnpackShape, cus, (int64_t)D.rows, kUpWaves);
   return launch("k_unpack", k_unpack, dim3(grid), dim3(kUpThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
                 row_src);
+}
+
+// Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic
+// LDS: what the occupancy query allows, at most MOE_LL_BLOCKS_PER_CU.  On
+// MI355X the first wave of this launch holds 6 per CU although the query
+// reports 7; with 7 per CU every 7th packer starts only after another has
+// finished, which costs more than it gains (measured at the decode shapes).
+#ifndef MOE_LL_BLOCKS_PER_CU
+#define MOE_LL_BLOCKS_PER_CU 6
+#endif
+static int ll_blocks_per_cu(size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find({dev, lds});
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(k_dispatch_ll), kThreads, lds) !=
+          hipSuccess ||
+      nb < 1)
+    nb = 1;
+  if (nb > MOE_LL_BLOCKS_PER_CU) nb = MOE_LL_BLOCKS_PER_CU;
+  cache[{dev, lds}] = nb;
+  return nb;
+}
+
+int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos,
+                       uint8_t* recv_q, float* recv_s, int cus, hipStream_t st) {
+  if (D0.B != 1 || D0.N * D0.T == 0) return MOE_EINVAL;
+  Dims D = D0;
+  D.slices = pack_slices(D, cus, x != nullptr);
+  size_t lds = count_lds_bytes(D.E);
+  lds = lds > cross_ll_lds_bytes(D.E) ? lds : cross_ll_lds_bytes(D.E);
+  lds = lds > pack_lds_bytes(D.NB) ? lds : pack_lds_bytes(D.NB);
+  // Packers: as many as the k_pack grid would have, but no more than fit on
+  // the GPU beside the N + 1 layout workgroups, so no packer starts late.
+  int npack = 0;
+  if (x) {
+    const int resident = cus * ll_blocks_per_cu(lds) - (D.N + 1);
+    npack = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
+    if (resident >= 1 && npack > resident) npack = resident;
+  }
+  return launch("k_dispatch_ll", k_dispatch_ll, dim3(D.N + 1 + npack), dim3(kThreads), lds, st, D, W, x, idx,
+                send_pos, recv_q, recv_s, npack);
 }
 
 }  // namespace moe

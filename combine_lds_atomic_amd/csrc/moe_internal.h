@@ -76,7 +76,62 @@ struct Ws {
   int *exp_off;       // [N][L+1]
   int *src_in_exp;    // [N+1][E] rows of expert e from sources before s
   int *local;         // [N][T*k] rank of each slot inside its chunk (several chunks per rank)
+  // Exchange area of the single-launch dispatch, present only when every
+  // rank's slots fit one routing chunk.  Each entry is an 8-byte pair
+  // (tag << 32 | value), published and read with single-copy-atomic stores
+  // and loads at agent scope, so a reader that sees the tag of the current
+  // call also sees that call's value and needs no fence.
+  uint32_t *ctl;      // [kCtlGroups + 1][kCtlStride]: per-group finish counter and call number, then the
+                      // count of finished groups
+  uint64_t *tpos;     // [N*T*k] send positions
+  uint64_t *toff;     // [N][N+1] send_off[s][d*L], [s][N] = valid slots of s
+  uint64_t *tcnt;     // [N][E] counts
+  uint64_t *trel;     // [N][N] recv_off[d][s] - send_off[s][d*L]
+  uint64_t *tbase;    // [N] region bases
+  uint64_t *tready;   // [kReadyCopies][kReadyStride]: published after the values packers need
 };
+
+// Copies of the "ready" word, one per 64-byte line, so that the waiting
+// workgroups spread their polls over many addresses.
+constexpr int kReadyCopies = 64;
+constexpr int kReadyStride = 8;
+
+// Control words of the single-launch dispatch.  Workgroup b belongs to group
+// b % kCtlGroups; each group has its own 64-byte line holding the number of
+// its workgroups that have finished and its copy of the call number (calls
+// completed on this workspace), so no single address takes one atomic per
+// workgroup.  Line kCtlGroups counts the groups that have finished.
+constexpr int kCtlGroups = 16;
+constexpr int kCtlStride = 16;   // uint32 words per line
+
+// Tag of call number `epoch`: the top bit is set, so no plain table entry
+// (non-negative, or -1) and no zeroed word ever looks like a tag.
+__device__ __forceinline__ uint32_t epoch_tag(uint32_t epoch) { return 0x80000000u | (epoch % 0x7FFFFFFFu); }
+
+__device__ __forceinline__ void tag_put(uint64_t* p, uint32_t tag, int v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tag_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_ok(uint64_t u, uint32_t tag) { return (uint32_t)(u >> 32) == tag; }
+
+// Upper bound on polls of one value; about a second at the longest, after
+// which the reader gives up, sets MOE_FLAG_TIMEOUT and drops what depended
+// on the value, so every wait ends.
+constexpr int kSpinLimit = 1 << 21;
+
+// Wait for a tagged value; false after kSpinLimit polls.
+__device__ __forceinline__ bool tag_wait(const uint64_t* p, uint32_t tag, int* v) {
+  uint64_t u = tag_load(p);
+  for (int it = 0; !tag_ok(u, tag); ++it) {
+    if (it == kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(2);
+    u = tag_load(p);
+  }
+  *v = (int)(uint32_t)u;
+  return true;
+}
 
 // ------------------------------------------------------------------ helpers
 
@@ -235,6 +290,8 @@ int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, c
                      hipStream_t st);
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st);
+int launch_dispatch_ll(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos,
+                       uint8_t* recv_q, float* recv_s, int cus, hipStream_t st);
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 

@@ -68,6 +68,8 @@ extern "C" {
 #define MOE_FLAG_BADID 1u    /* a top-k id outside [0, E): that slot was dropped  */
 #define MOE_FLAG_OVERFLOW 2u /* a fixed region got more rows than region_rows     */
 #define MOE_FLAG_BOUND 4u    /* a region count exceeded N*T*max(k, E/N)           */
+#define MOE_FLAG_TIMEOUT 8u  /* moe_dispatch_send_ll: a wait inside the launch gave
+                                up (its rows were dropped); re-initialise ws     */
 
 /*
  * Problem shape, per logical rank, identical on all N ranks.
@@ -99,8 +101,10 @@ int64_t moe_recv_rows(const moe_shape *shape);
  * bases and the sticky error word. */
 int64_t moe_workspace_bytes(const moe_shape *shape);
 
-/* Zero the workspace header (the error word).  Call once after
- * allocating a workspace, before its first use.  ws: device, 256-B aligned. */
+/* Zero the workspace header (the error word) and, when every rank fits one
+ * routing chunk (T*k <= 4096), the exchange area of moe_dispatch_send_ll.
+ * Call once after allocating a workspace, before its first use, and again
+ * before using it for another shape.  ws: device, 256-B aligned. */
 int moe_workspace_init(const moe_shape *shape, void *ws, void *stream);
 
 /*
@@ -126,6 +130,27 @@ int moe_workspace_init(const moe_shape *shape, void *ws, void *stream);
  */
 int moe_dispatch_send(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx,
                       uint8_t *recv_q, float *recv_s, int32_t *send_pos, void *ws, void *stream);
+
+/*
+ * Dispatch, send half, in ONE kernel launch (AWS China blog "750B MoE model
+ * migration from a self-built RoCE cluster to AWS EFA", section 4.4, DeepEP
+ * low-latency mode: the whole dispatch in a single kernel with no CPU
+ * involvement, for small decode batches).  Same arguments and the same
+ * results, bit for bit, as moe_dispatch_send, including every table that
+ * moe_dispatch_recv, moe_combine_pull and moe_layout_export read from ws.
+ * Counting, the count exchange, the scans and the quantised stores run in
+ * one grid; workgroups hand values to each other through ws (each value
+ * tagged with a per-workspace call number that the launch advances), so:
+ *   - every rank's slots must fit one routing chunk: T*k <= 4096, else
+ *     MOE_EINVAL (use moe_dispatch_send);
+ *   - ws must have been initialised by moe_workspace_init for this shape;
+ *     calls on one workspace must not overlap (one stream);
+ *   - every wait inside the launch is bounded; a wait that gives up sets
+ *     MOE_FLAG_TIMEOUT and drops the rows that depended on it (never seen in
+ *     correct use; re-initialise ws afterwards).
+ */
+int moe_dispatch_send_ll(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx,
+                         uint8_t *recv_q, float *recv_s, int32_t *send_pos, void *ws, void *stream);
 
 /*
  * Dispatch, receive half ("Dispatch and combine": the receive buffer is

@@ -24,8 +24,10 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
 
 
 def run_all(cfg: W.Config, T: int, region_rows: int = 0, idx=None, w=None, x=None, y=None,
-            payload: bool = True, combine: bool = True, fill: int | None = 0x5A, device="cuda"):
-    """Generate (or take) inputs and run dispatch send/recv and combine send/recv."""
+            payload: bool = True, combine: bool = True, fill: int | None = 0x5A, device="cuda",
+            single_launch: bool = False):
+    """Generate (or take) inputs and run dispatch send/recv and combine send/recv
+    (single_launch: the send half through moe_dispatch_send_ll)."""
     sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, region_rows)
     if idx is None:
         idx, w = W.routing(cfg, T)
@@ -34,7 +36,8 @@ def run_all(cfg: W.Config, T: int, region_rows: int = 0, idx=None, w=None, x=Non
     if x is None and payload:
         x = W.tokens(cfg, device, T)
     B = moe.allocate(sh, device, payload=payload, combine=combine, fill_rows=fill)
-    moe.moe_dispatch_send(sh, x if payload else None, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
+    send = moe.moe_dispatch_send_ll if single_launch else moe.moe_dispatch_send
+    send(sh, x if payload else None, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
     moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
     if combine:
         if y is None:

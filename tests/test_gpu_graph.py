@@ -1,7 +1,8 @@
-"""The four calls (and the pulling combine) are capturable in a HIP graph: no
-host synchronisation, allocation or memset happens inside them.  A captured
-step is replayed several times, with eager work and synchronisation between
-replays, and every replay must equal the eager run bit for bit."""
+"""The four calls (and the pulling combine, and the single-launch dispatch) are
+capturable in a HIP graph: no host synchronisation, allocation or memset
+happens inside them.  A captured step is replayed several times, with eager
+work and synchronisation between replays, and every replay must equal the
+eager run bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -11,8 +12,9 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 128), ("dsv3_decode", 128)])
-def test_graph_replay_matches_eager(name, T):
+@pytest.mark.parametrize("name,T,single_launch", [("tiny", 128, False), ("dsv3_decode", 128, False),
+                                                   ("tiny", 128, True), ("dsv3_decode", 128, True)])
+def test_graph_replay_matches_eager(name, T, single_launch):
     import combine_lds_atomic_amd as moe
     cfg = W.CONFIGS[name]
     sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k)
@@ -23,8 +25,10 @@ def test_graph_replay_matches_eager(name, T):
     y = W.expert_outputs(cfg, B.rows, "cuda")
     out_pull = torch.empty_like(B.out)
 
+    send = moe.moe_dispatch_send_ll if single_launch else moe.moe_dispatch_send
+
     def step():
-        moe.moe_dispatch_send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
+        send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws)
         moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
         moe.moe_combine_send(sh, y, B.row_src, B.ws, B.comb)
         moe.moe_combine_recv(sh, B.comb, B.send_pos, w_d, B.out)
