@@ -390,3 +390,75 @@ def combine_rows(y_rows, w_rows):
     for j in range(y_rows.shape[0]):
         acc = (acc + (np.float32(w_rows[j]) * bf16_from_bits(y_rows[j])).astype(np.float32)).astype(np.float32)
     return bf16_bits(bf16_round(acc))
+
+
+# ---------------------------------------------------------------------------
+# Combine with send-side partial accumulation
+# ---------------------------------------------------------------------------
+# [EFA] "Evaluation: dispatch/combine latency": accumulating a token's rows on
+# the send side of combine reduces the data transferred, possibly at some cost
+# in accuracy.  Readings (the page gives the idea, not the arithmetic):
+#   * a group is the set of a token's slots whose rows sit on one destination
+#     rank (owner(e) = e // L), counting only slots that have an expert-major
+#     row; the group's first slot is its leader;
+#   * the sending (expert) rank sums the group in float32 in slot order,
+#     acc = fl32(acc + fl32(w_j * y_j)) with no fused multiply-add (the
+#     weights travel with the token), and ships bf16_rne(acc) as one row,
+#     stored where the leader's row would return (s*T*k + send_pos of the
+#     leader);
+#   * the receiving (source) rank adds the group rows in float32 in leader
+#     order and rounds once: out = bf16_rne(sum_g float(p_g)).
+
+def partial_token(y_rows, w_rows, dest, part):
+    """One token.  y_rows uint16 [k, H] bfloat16 bits in slot order, w_rows
+    float32 [k], dest int [k] the rank holding each slot's row, part bool [k]
+    whether the slot has a row.
+
+    Returns (groups, out): groups is a list of (leader slot, p uint16 [H]) in
+    leader order; out uint16 [H]."""
+    k, H = y_rows.shape
+    groups = []
+    done = set()
+    for j in range(k):
+        if not part[j] or dest[j] in done:
+            continue
+        done.add(dest[j])
+        acc = np.zeros(H, np.float32)
+        for m in range(j, k):
+            if part[m] and dest[m] == dest[j]:
+                term = (np.float32(w_rows[m]) * bf16_from_bits(y_rows[m])).astype(np.float32)
+                acc = (acc + term).astype(np.float32)
+        groups.append((j, bf16_bits(bf16_round(acc))))
+    acc = np.zeros(H, np.float32)
+    for _, p in groups:
+        acc = (acc + bf16_from_bits(p)).astype(np.float32)
+    return groups, bf16_bits(bf16_round(acc))
+
+
+def combine_partial(y_em, idx, lay: Layout, w):
+    """Send-side partial combine of every token.  y_em uint16 [rows, H]
+    (expert-major bfloat16 bits), idx [N, T, k], w float32 [N, T, k].
+
+    Returns (comb, lead, out): comb uint16 [N*T*k, H] holds each group's row
+    at its leader's return position (other rows zero; the library leaves
+    them untouched), lead bool [N, T, k] marks leaders, out uint16 [N, T, H]."""
+    N, T, k = lay.N, lay.T, lay.k
+    H = y_em.shape[1]
+    idx = np.asarray(idx, np.int64)
+    w = np.asarray(w, np.float32)
+    part = lay.em_row >= 0
+    dest = np.where(lay.slot_valid, idx, 0) // lay.L
+    comb = np.zeros((N * T * k, H), np.uint16)
+    lead = np.zeros((N, T, k), bool)
+    out = np.zeros((N, T, H), np.uint16)
+    for s in range(N):
+        for t in range(T):
+            rows = np.zeros((k, H), np.uint16)
+            pj = part[s, t]
+            rows[pj] = y_em[lay.em_row[s, t][pj]]
+            groups, out[s, t] = partial_token(rows, w[s, t], dest[s, t], pj)
+            for j, p in groups:
+                lead[s, t, j] = True
+                comb[s * T * k + lay.send_pos[s, t, j]] = p
+    return comb, lead, out
+

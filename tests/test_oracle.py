@@ -393,3 +393,174 @@ def test_combine_skips_dropped_slots():
     out = O.bf16_from_bits(O.combine_recv(comb, lay.send_pos, w, T, k))
     ref = O.bf16_round((np.float32(0.5) * O.bf16_from_bits(comb[lay.send_pos[0, 0, 0]])).astype(np.float32))
     assert (out[0, 0] == ref).all()
+
+
+# ---------------------------------------------------------------- combine with send-side partial sums
+
+def _partial_case(idx, w, y_token_values, H, E):
+    """Rows of constant value per slot, placed in expert-major order."""
+    idx = np.asarray(idx)
+    N, T, k = idx.shape
+    lay = O.layout(idx, E, N, 0)
+    y = np.zeros((lay.total_rows, H), np.uint16)
+    vals = np.asarray(y_token_values, np.float32)
+    for s in range(N):
+        for t in range(T):
+            for j in range(k):
+                if lay.em_row[s, t, j] >= 0:
+                    y[lay.em_row[s, t, j]] = O.bf16_bits(np.full(H, vals[s, t, j], np.float32))
+    return lay, y
+
+
+def test_partial_golden_example():
+    g = _load("combine_partial_example.json")
+    lay, y = _partial_case(g["idx"], g["w"], g["y_slot_values"], g["H"], g["E"])
+    w = np.asarray(g["w"], np.float32)
+    comb, lead, out = O.combine_partial(y, g["idx"], lay, w)
+    assert (lead == np.asarray(g["group_leaders"])).all()
+    for s, rows in g["group_rows_bits"].items():
+        for j, bits in rows.items():
+            s_, j_ = int(s), int(j)
+            assert (comb[s_ * g["T"] * g["k"] + lay.send_pos[s_, 0, j_]] == bits).all(), (s, j)
+    assert (out[:, 0, :] == np.asarray(g["out_partial_bits"])).all()
+    plain = O.combine_recv(O.combine_send(y, O.row_src(lay), g["N"], g["T"], g["k"]), lay.send_pos, w, g["T"], g["k"])
+    assert (plain[:, 0, :] == np.asarray(g["out_plain_bits"])).all()
+
+
+def test_partial_equals_plain_when_a_token_uses_one_rank():
+    """All of a token's experts on one rank: one group, whose bf16 row is the
+    plain combine's result, and re-rounding it changes nothing."""
+    rng = np.random.default_rng(21)
+    N, T, H, E, k = 4, 12, 256, 32, 4            # L = 8 experts per rank >= k
+    L = E // N
+    idx = np.zeros((N, T, k), np.int64)
+    for s in range(N):
+        for t in range(T):
+            d = rng.integers(0, N)
+            idx[s, t] = d * L + rng.choice(L, k, replace=False)
+    lay = O.layout(idx, E, N, 0)
+    w = rng.dirichlet(np.ones(k), (N, T)).astype(np.float32)
+    y = O.bf16_bits(_bf16_rows(rng, lay.total_rows, H))
+    comb, lead, out = O.combine_partial(y, idx, lay, w)
+    assert (lead.sum(axis=2) == 1).all() and lead[:, :, 0].all()
+    plain = O.combine_recv(O.combine_send(y, O.row_src(lay), N, T, k), lay.send_pos, w, T, k)
+    assert (out == plain).all()
+
+
+def test_partial_singleton_groups_closed_form():
+    """One expert per rank (E = N), distinct experts per token: every slot is
+    its own group, so out = bf16(sum_j bf16(fl32(w_j * y_j))) in slot order."""
+    rng = np.random.default_rng(22)
+    N, T, H, k = 6, 10, 128, 4
+    idx = np.stack([np.stack([rng.choice(N, k, replace=False) for _ in range(T)]) for _ in range(N)])
+    lay = O.layout(idx, N, N, 0)
+    w = rng.dirichlet(np.ones(k), (N, T)).astype(np.float32)
+    y = O.bf16_bits(_bf16_rows(rng, lay.total_rows, H))
+    _, lead, out = O.combine_partial(y, idx, lay, w)
+    assert lead.all()
+    yv = O.bf16_from_bits(y[lay.em_row])                               # [N, T, k, H]
+    p = O.bf16_round((w[..., None] * yv).astype(np.float32))
+    acc = np.zeros((N, T, H), np.float32)
+    for j in range(k):
+        acc = (acc + p[:, :, j]).astype(np.float32)
+    assert (out == O.bf16_bits(O.bf16_round(acc))).all()
+
+
+def test_partial_unit_and_one_hot_weights_are_exact():
+    rng = np.random.default_rng(23)
+    N, T, H, E, k = 4, 16, 128, 16, 4
+    idx = _random_idx(rng, N, T, E, k)
+    lay = O.layout(idx, E, N, 0)
+    y = O.bf16_bits(_bf16_rows(rng, lay.total_rows, H))
+    pick = rng.integers(0, k, (N, T))
+    w = np.zeros((N, T, k), np.float32)
+    np.put_along_axis(w, pick[:, :, None], 1.0, axis=2)
+    _, _, out = O.combine_partial(y, idx, lay, w)
+    for s in range(N):
+        for t in range(T):
+            assert (out[s, t] == y[lay.em_row[s, t, pick[s, t]]]).all()
+
+
+def test_partial_groups_are_the_distinct_ranks_of_a_token():
+    rng = np.random.default_rng(24)
+    N, T, H, E, k = 4, 30, 128, 16, 6
+    idx = _random_idx(rng, N, T, E, k)
+    idx[0, 0, 2] = 99                                                  # a dropped slot
+    lay = O.layout(idx, E, N, 0)
+    y = O.bf16_bits(_bf16_rows(rng, lay.total_rows, H))
+    w = rng.dirichlet(np.ones(k), (N, T)).astype(np.float32)
+    _, lead, _ = O.combine_partial(y, idx, lay, w)
+    L = E // N
+    for s in range(N):
+        for t in range(T):
+            ranks = [int(e) // L for e in idx[s, t] if 0 <= e < E]
+            assert lead[s, t].sum() == len(set(ranks))
+            for j in np.flatnonzero(lead[s, t]):                      # a leader is its rank's first slot
+                assert [int(e) // L for e in idx[s, t][:j] if 0 <= e < E].count(int(idx[s, t, j]) // L) == 0
+
+
+def test_partial_fp64_error_bound():
+    """|out - sum_j w_j y_j| <= 2^-8 (|out| + sum_g |p_g|) + 2k 2^-24 sum_j |w_j y_j|:
+    one bf16 rounding of each group row and of the result, float32 sums."""
+    rng = np.random.default_rng(25)
+    N, T, H, E, k = 4, 20, 128, 16, 6
+    idx = _random_idx(rng, N, T, E, k)
+    lay = O.layout(idx, E, N, 0)
+    y = O.bf16_bits(_bf16_rows(rng, lay.total_rows, H))
+    w = rng.dirichlet(np.ones(k), (N, T)).astype(np.float32)
+    comb, lead, out = O.combine_partial(y, idx, lay, w)
+    outf = O.bf16_from_bits(out).astype(np.float64)
+    worst = 0.0
+    for s in range(N):
+        for t in range(T):
+            rows = O.bf16_from_bits(y[lay.em_row[s, t]]).astype(np.float64)        # [k, H]
+            ww = w[s, t].astype(np.float64)[:, None]
+            exact = (ww * rows).sum(axis=0)
+            mag = (np.abs(ww) * np.abs(rows)).sum(axis=0)
+            pg = sum(np.abs(O.bf16_from_bits(comb[s * T * k + lay.send_pos[s, t, j]]).astype(np.float64))
+                     for j in np.flatnonzero(lead[s, t]))
+            lim = 2.0 ** -8 * (np.abs(outf[s, t]) + pg) + 2 * k * 2.0 ** -24 * mag + 2.0 ** -133
+            err = np.abs(outf[s, t] - exact)
+            assert (err <= lim).all()
+            worst = max(worst, float((err / lim).max()))
+    assert worst > 0.05          # the bound is not vacuous: some elements come near it
+
+
+def test_partial_receive_sums_in_leader_order():
+    """Groups are added in leader (slot) order: with rows 2^24, 1, -2^24 on three
+    ranks and unit weights, float32 gives (2^24 + 1) - 2^24 = 0 in that order
+    (2^24 + 1 rounds to 2^24) but 1 in the reverse order."""
+    idx = np.array([[[0, 1, 2]], [[1, 2, 0]], [[2, 0, 1]]])       # N = E = 3: every slot its own group
+    vals = np.array([[[2.0 ** 24, 1.0, -2.0 ** 24]]] * 3, np.float32)
+    lay, y = _partial_case(idx, np.ones((3, 1, 3), np.float32), vals, 128, 3)
+    _, lead, out = O.combine_partial(y, idx, lay, np.ones((3, 1, 3), np.float32))
+    assert lead.all()
+    assert (O.bf16_from_bits(out) == 0.0).all()
+
+
+def test_partial_slots_without_a_row_take_no_part():
+    """A slot whose row a full fixed region dropped behaves like a dropped id:
+    the same leaders and the same output as the routing with that id removed."""
+    rng = np.random.default_rng(26)
+    N, T, H, E, k = 4, 24, 128, 8, 3
+    idx = _random_idx(rng, N, T, E, k)
+    idx[:, :, 0] = 0                                           # every token's slot 0 -> rank 0
+    R = int(O.layout(idx, E, N).recv_total.max()) - 9
+    lay = O.layout(idx, E, N, R)
+    assert lay.flags & O.FLAG_OVERFLOW
+    gone = lay.slot_valid & (lay.em_row < 0)
+    assert gone.any()
+    w = rng.dirichlet(np.ones(k), (N, T)).astype(np.float32)
+    vals = rng.standard_normal((N, T, k)).astype(np.float32)
+    lay_r, y_r = _partial_case(np.where(gone, -1, idx), w, vals, H, E)
+    y = np.zeros((lay.total_rows, H), np.uint16)
+    for s in range(N):
+        for t in range(T):
+            for j in range(k):
+                if lay.em_row[s, t, j] >= 0:
+                    y[lay.em_row[s, t, j]] = O.bf16_bits(np.full(H, vals[s, t, j], np.float32))
+    _, lead, out = O.combine_partial(y, idx, lay, w)
+    _, lead_r, out_r = O.combine_partial(y_r, np.where(gone, -1, idx), lay_r, w)
+    assert (lead == lead_r).all() and (out == out_r).all()
+    assert not (lead & gone).any()
+
