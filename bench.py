@@ -10,8 +10,10 @@ shape: dispatch 128, combine 4096 tokens per rank) time the dispatch at the
 dispatch batch and the combine on the layout of an untimed, payload-free
 dispatch at the combine batch.
 
-The pulling combine (moe_combine_pull) is timed after the steps, on the same
-data, and reported beside them; it is not part of the step.  So is, when every
+The pulling combine (moe_combine_pull) and the combine with send-side partial
+sums (moe_combine_send_partial + moe_combine_recv_partial) are timed after the
+steps, on the same data, and reported beside them; they are not part of the
+step.  So is, when every
 rank's slots fit one routing chunk (T*k <= 4096), the step with the
 single-launch moe_dispatch_send_ll in place of moe_dispatch_send.
 
@@ -35,20 +37,34 @@ KERNEL_OF = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_se
              "combine_recv": "k_comb_recv"}
 
 
-def algorithmic_bytes(N, T, H, E, k, Tc=None):
+def algorithmic_bytes(N, T, H, E, k, Tc=None, G=None):
     """Bytes each phase must move (inputs read once, outputs written once);
-    Tc is the combine batch when it differs from the dispatch batch T."""
+    Tc is the combine batch when it differs from the dispatch batch T; G the
+    number of (token, destination rank) groups of the combine batch, which
+    the send-side partial combine ships one row each."""
     Tc = T if Tc is None else Tc
     P, Pc = N * T * k, N * Tc * k
+    G = Pc if G is None else G
     rowq = H + 4 * (H // 128)          # fp8 payload + fp32 scales
     rowb = 2 * H                       # bf16 row
     return {
+        "combine_send_partial": Pc * rowb + G * rowb + 3 * N * Tc * k * 4,
+        "combine_recv_partial": G * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
         "dispatch_send": N * T * 2 * H + P * rowq + 2 * N * T * k * 4 + N * E * 4,
         "dispatch_recv": 2 * P * rowq,
         "combine_send": 2 * Pc * rowb,
         "combine_recv": Pc * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
         "combine_pull": Pc * rowb + N * Tc * H * 2 + 3 * N * Tc * k * 4,
     }
+
+
+def combine_groups(idx, L):
+    """(token, destination rank) groups of a routing [N, T, k] with valid ids:
+    the rows the send-side partial combine ships."""
+    import numpy as np
+    k = idx.shape[-1]
+    ranks = np.sort(np.asarray(idx).reshape(-1, k) // L, axis=1)
+    return int(ranks.shape[0] + np.count_nonzero(ranks[:, 1:] != ranks[:, :-1]))
 
 
 def _kernel_sources_digest():
@@ -148,6 +164,7 @@ def main():
         moe.moe_dispatch_recv(shc, None, None, Bc.ws, None, None, Bc.exp_off, Bc.row_src)
     y = W.expert_outputs(cfg, Bc.rows, dev)
     out_pull = torch.empty_like(Bc.out)
+    G = combine_groups(idx if Tc == T else idxc, cfg.E // cfg.N)
 
     def step(ev=None, send=moe.moe_dispatch_send):
         if ev: ev[0].record(stream)
@@ -179,7 +196,7 @@ def main():
     per_phase_ms = ms.mean(axis=0)
     p90_ms = np.percentile(ms, 90, axis=0)
     step_ms = wall * 1e3 / args.steps
-    nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k, Tc)
+    nbytes = algorithmic_bytes(cfg.N, T, cfg.H, cfg.E, cfg.k, Tc, G)
     total = sum(nbytes[p] for p in PHASES)
 
     # The same step captured once in a HIP graph and replayed (no launch gaps).
@@ -243,6 +260,26 @@ def main():
     pull_ms = np.array([pull_ev[i].elapsed_time(pull_ev[i + 1]) for i in range(args.steps)]).mean()
     pull_same = bool(torch.equal(out_pull.view(torch.int16), Bc.out.view(torch.int16)))
 
+    # Combine with send-side partial sums (one row per token and destination
+    # rank), on the same data, into its own buffers (not part of the step).
+    comb_p = torch.empty_like(Bc.comb)
+    out_p = torch.empty_like(Bc.out)
+    for _ in range(2):
+        moe.moe_combine_send_partial(shc, y, idxc_d, Bc.send_pos, wc_d, Bc.ws, comb_p)
+        moe.moe_combine_recv_partial(shc, comb_p, idxc_d, Bc.send_pos, Bc.ws, out_p)
+    part_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        part_ev[i][0].record(stream)
+        moe.moe_combine_send_partial(shc, y, idxc_d, Bc.send_pos, wc_d, Bc.ws, comb_p)
+        part_ev[i][1].record(stream)
+        moe.moe_combine_recv_partial(shc, comb_p, idxc_d, Bc.send_pos, Bc.ws, out_p)
+        part_ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    part_ms = np.array([[part_ev[i][p].elapsed_time(part_ev[i][p + 1]) for p in range(2)]
+                        for i in range(args.steps)]).mean(axis=0)
+    part_diff = float((out_p.view(torch.int16) != Bc.out.view(torch.int16)).float().mean().item())
+    del comb_p
+
     # Achievable read+write rate: a plain copy of the dominant phase's bytes.
     dom = max(range(4), key=lambda p: per_phase_ms[p])
     copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
@@ -303,6 +340,11 @@ def main():
         "combine_frac": round((nbytes["combine_send"] + nbytes["combine_recv"]) /
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
+        "combine_partial": {"groups_per_token": round(G / (cfg.N * Tc), 3),
+                            "send": info("combine_send_partial", part_ms[0]),
+                            "recv": info("combine_recv_partial", part_ms[1]),
+                            "us": round((part_ms[0] + part_ms[1]) * 1e3, 1),
+                            "elements_differing_from_send_recv": round(part_diff, 5)},
         "graph_step_us": round(graph_step_ms * 1e3, 1),
         "single_launch_dispatch": single,
         "copy_ceiling_GB/s": round(copy_gbs, 1),

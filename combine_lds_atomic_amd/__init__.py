@@ -76,6 +76,8 @@ _SIG = {
     "moe_combine_send": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "moe_combine_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "moe_combine_pull": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_send_partial": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_recv_partial": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "moe_layout_export": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
     "moe_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
@@ -157,6 +159,18 @@ def moe_combine_recv(sh, comb, send_pos, topk_w, out, stream=None):
 def moe_combine_pull(sh, y_em, topk_idx, send_pos, topk_w, ws, out, stream=None):
     _check("moe_combine_pull", lib.moe_combine_pull(ctypes.byref(sh), _ptr(y_em), _ptr(topk_idx), _ptr(send_pos),
                                                     _ptr(topk_w), _ptr(ws), _ptr(out), _stream(stream)))
+
+
+def moe_combine_send_partial(sh, y_em, topk_idx, send_pos, topk_w, ws, comb, stream=None):
+    _check("moe_combine_send_partial", lib.moe_combine_send_partial(ctypes.byref(sh), _ptr(y_em), _ptr(topk_idx),
+                                                                    _ptr(send_pos), _ptr(topk_w), _ptr(ws),
+                                                                    _ptr(comb), _stream(stream)))
+
+
+def moe_combine_recv_partial(sh, comb, topk_idx, send_pos, ws, out, stream=None):
+    _check("moe_combine_recv_partial", lib.moe_combine_recv_partial(ctypes.byref(sh), _ptr(comb), _ptr(topk_idx),
+                                                                    _ptr(send_pos), _ptr(ws), _ptr(out),
+                                                                    _stream(stream)))
 
 
 def moe_status(ws, stream=None) -> int:

@@ -253,6 +253,37 @@ int moe_combine_pull(const moe_shape* shape, const uint16_t* y_em, const int32_t
   return launch_comb_pull(D, W, y_em, topk_idx, send_pos, topk_w, out, device_cus(), as_stream(stream));
 }
 
+int moe_combine_send_partial(const moe_shape* shape, const uint16_t* y_em, const int32_t* topk_idx,
+                             const int32_t* send_pos, const float* topk_w, const void* ws, uint16_t* comb,
+                             void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  if (D.T == 0) return MOE_OK;
+  if (!y_em || !topk_idx || !send_pos || !topk_w || !comb) return MOE_ENULL;
+  if (!aligned(y_em, 16) || !aligned(comb, 16) || !aligned(topk_idx, 4) || !aligned(send_pos, 4) ||
+      !aligned(topk_w, 4))
+    return MOE_EALIGN;
+  return launch_comb_send_partial(D, W_of(D, const_cast<void*>(ws)), y_em, topk_idx, send_pos, topk_w, comb,
+                                  device_cus(), as_stream(stream));
+}
+
+int moe_combine_recv_partial(const moe_shape* shape, const uint16_t* comb, const int32_t* topk_idx,
+                             const int32_t* send_pos, const void* ws, uint16_t* out, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  if (D.T == 0) return MOE_OK;
+  if (!comb || !topk_idx || !send_pos || !out) return MOE_ENULL;
+  if (!aligned(comb, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(send_pos, 4)) return MOE_EALIGN;
+  return launch_comb_recv_partial(D, W_of(D, const_cast<void*>(ws)), comb, topk_idx, send_pos, out, device_cus(),
+                                  as_stream(stream));
+}
+
 int moe_status(void* ws, void* stream, uint32_t* flags) {
   if (!ws || !flags) return MOE_ENULL;
   if (!aligned(ws, kAlign)) return MOE_EALIGN;

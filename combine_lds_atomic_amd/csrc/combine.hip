@@ -4,11 +4,18 @@
 // routing is already known from dispatch, rows go back with one contiguous
 // write per peer and the receive side accumulates them into the output).
 //
-//   k_comb_send  each workgroup streams a contiguous range of expert-major
-//                rows: comb[row_src[i]] = y[i]
-//   k_comb_recv  each workgroup streams a contiguous range of tokens: fp32
-//                sum over slots of w * y, bf16 out
-//   k_copy16     plain streaming copy (measurement aid)
+//   k_comb_send          each workgroup streams a contiguous range of
+//                        expert-major rows: comb[row_src[i]] = y[i]
+//   k_comb_recv          each workgroup streams a contiguous range of
+//                        tokens: fp32 sum over slots of w * y, bf16 out
+//   k_comb_pull          the same sum, rows read in place (expert-major)
+//   k_comb_send_partial  send-side partial sums: one bf16 row per (token,
+//                        destination rank) group ("Evaluation:
+//                        dispatch/combine latency": accumulating on the send
+//                        side cuts the data sent)
+//   k_comb_recv_partial  the receive side of it: fp32 sum of a token's group
+//                        rows, bf16 out
+//   k_copy16             plain streaming copy (measurement aid)
 #include "moe_internal.h"
 
 namespace moe {
@@ -77,11 +84,40 @@ constexpr int kSlotGroup = 8;
 #endif
 constexpr int kCombPieces = MOE_COMB_PIECES;   // 1 KB pieces read per slot row per step
 
-// The weighted sum of one combine, token by token.  PULL = false: slot rows
-// are rank s's returned rows comb[s*T*k + send_pos].  PULL = true: they are
-// read where the expert wrote them, y_em[base[d] + expert-major index], found
-// from the routing tables (the row combine_send would have copied).
-template <bool PULL>
+// Expert-major row of a slot of source s with expert e and sender position
+// sp, found from the routing tables: the row combine_send would copy back.
+// -1 for a bad id, or a row that a full fixed region dropped.
+__device__ __forceinline__ int em_row_of(const Dims& D, const Ws& W, int s, int e, int sp) {
+  if (e < 0 || e >= D.E || sp < 0 || sp >= D.TK) return -1;
+  const int d = e / D.L, l = e - d * D.L;
+  const int* so = W.send_off + s * (D.E + 1);
+  const int u = sp - so[e];                                                         // index inside (s, e)
+  const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;      // expert-major
+  const int j = W.recv_off[d * (D.N + 1) + s] + (so[e] - so[d * D.L]) + u;         // source-major
+  const int p = W.base[d] + i;
+  return (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) ? p : -1;
+}
+
+// Per lane j < k: whether slot j leads its group, i.e. has a row (dest >= 0)
+// and no earlier slot of the token has a row on the same rank.
+__device__ __forceinline__ bool group_leader(int dest, int k, int lane) {
+  bool lead = dest >= 0;
+  for (int jj = 0; jj < k; ++jj) {
+    const int dj = __builtin_amdgcn_readlane(dest, jj);
+    if (jj < lane && dj == dest) lead = false;
+  }
+  return lead;
+}
+
+enum class CombMode { kRecv, kPull, kRecvPartial };
+
+// The weighted sum of one combine, token by token.
+//   kRecv: slot rows are rank s's returned rows comb[s*T*k + send_pos];
+//   kPull: they are read where the expert wrote them, y_em[base[d] +
+//          expert-major index], found from the routing tables;
+//   kRecvPartial: only group leaders contribute, with weight 1, their rows
+//          comb[s*T*k + send_pos] holding the group's partial sum.
+template <CombMode MODE>
 __device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
                                                const int* __restrict__ idx, const int* __restrict__ send_pos,
                                                const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
@@ -92,22 +128,22 @@ __device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const
     const int s = tok / D.T;
     int row = -1;
     float wt = 0.0f;
-    if (lane < D.k) {
+    if (MODE == CombMode::kRecvPartial) {
+      int dest = -1, sp = -1;
+      if (lane < D.k) {
+        sp = send_pos[(int64_t)tok * D.k + lane];
+        const int e = idx[(int64_t)tok * D.k + lane];
+        if (em_row_of(D, W, s, e, sp) >= 0) dest = e / D.L;
+      }
+      if (group_leader(dest, D.k, lane) && lane < D.k) row = s * D.TK + sp;
+      wt = 1.0f;
+    } else if (lane < D.k) {
       const int sp = send_pos[(int64_t)tok * D.k + lane];
       wt = topk_w[(int64_t)tok * D.k + lane];
-      if (!PULL) {
+      if (MODE == CombMode::kRecv) {
         if (sp >= 0 && sp < D.TK) row = s * D.TK + sp;
       } else {
-        const int e = idx[(int64_t)tok * D.k + lane];
-        if (e >= 0 && e < D.E && sp >= 0 && sp < D.TK) {
-          const int d = e / D.L, l = e - d * D.L;
-          const int* so = W.send_off + s * (D.E + 1);
-          const int u = sp - so[e];                                          // index inside (s, e)
-          const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;   // expert-major
-          const int j = W.recv_off[d * (D.N + 1) + s] + (so[e] - so[d * D.L]) + u;     // source-major
-          const int p = W.base[d] + i;
-          if (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) row = p;
-        }
+        row = em_row_of(D, W, s, idx[(int64_t)tok * D.k + lane], sp);
       }
     }
     uint16_t* orow = out + (int64_t)tok * D.H;
@@ -165,7 +201,7 @@ __global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, Ws W, const ui
                                                            const int* __restrict__ send_pos,
                                                            const float* __restrict__ topk_w,
                                                            uint16_t* __restrict__ out) {
-  combine_tokens<false>(D, W, comb, nullptr, send_pos, topk_w, out);
+  combine_tokens<CombMode::kRecv>(D, W, comb, nullptr, send_pos, topk_w, out);
 }
 
 __global__ __launch_bounds__(kCrThreads) void k_comb_pull(Dims D, Ws W, const uint16_t* __restrict__ y,
@@ -173,7 +209,135 @@ __global__ __launch_bounds__(kCrThreads) void k_comb_pull(Dims D, Ws W, const ui
                                                            const int* __restrict__ send_pos,
                                                            const float* __restrict__ topk_w,
                                                            uint16_t* __restrict__ out) {
-  combine_tokens<true>(D, W, y, idx, send_pos, topk_w, out);
+  combine_tokens<CombMode::kPull>(D, W, y, idx, send_pos, topk_w, out);
+}
+
+__global__ __launch_bounds__(kCrThreads) void k_comb_recv_partial(Dims D, Ws W, const uint16_t* __restrict__ comb,
+                                                                   const int* __restrict__ idx,
+                                                                   const int* __restrict__ send_pos,
+                                                                   uint16_t* __restrict__ out) {
+  combine_tokens<CombMode::kRecvPartial>(D, W, comb, idx, send_pos, nullptr, out);
+}
+
+// bf16 bits of 8 float32 sums, packed for one 16-byte store.
+__device__ __forceinline__ v4u pack_bf16x8(const float* acc) {
+  v4u o;
+  o[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o[2] = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o[3] = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  return o;
+}
+
+// Send-side partial sums, token by token (one wave per token): for each
+// group (a token's slots whose rows sit on one rank) in leader order, its
+// members in slot order, acc = fl(acc + fl(w * y)) with no fused
+// multiply-add, rounded to bf16 and stored where the leader's row returns
+// (comb[s*T*k + send_pos of the leader]).  Each step covers 512 columns
+// (lane l holds 8 elements).  With k <= kSlotGroup (every benchmark shape)
+// a step loads all k rows at once and forms every group from registers;
+// larger k takes the groups one after another, loading each group's
+// members kSlotGroup at a time.  Either way every slot row is read once.
+constexpr int kSpWaves = kSendPartialShape.waves, kSpThreads = kSendPartialShape.threads();
+#ifndef MOE_SEND_PIECES
+#define MOE_SEND_PIECES 2
+#endif
+constexpr int kSendPieces = MOE_SEND_PIECES;
+__global__ __launch_bounds__(kSpThreads) void k_comb_send_partial(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                                   const int* __restrict__ idx,
+                                                                   const int* __restrict__ send_pos,
+                                                                   const float* __restrict__ topk_w,
+                                                                   uint16_t* __restrict__ comb) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  int lo, hi;
+  block_range(D.N * D.T, lo, hi);
+  for (int tok = lo + wv; tok < hi; tok += kSpWaves) {
+    const int s = tok / D.T;
+    int row = -1, dest = -1, sp = -1;
+    float wt = 0.0f;
+    if (lane < D.k) {
+      sp = send_pos[(int64_t)tok * D.k + lane];
+      wt = topk_w[(int64_t)tok * D.k + lane];
+      const int e = idx[(int64_t)tok * D.k + lane];
+      row = em_row_of(D, W, s, e, sp);
+      if (row >= 0) dest = e / D.L;
+    }
+    const bool lead = group_leader(dest, D.k, lane);
+    const int orow = lead ? s * D.TK + sp : -1;   // where a leader's group row goes
+    auto weight = [&](int j) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), j));
+    };
+    if (D.k <= kSlotGroup) {
+      // kSendPieces adjacent 512-column pieces per step: lane l holds
+      // elements [base + c*512 + 8l, +8) of piece c.
+      for (int base = 0; base < D.H; base += kWave * 8 * kSendPieces) {
+        v4u v[kSlotGroup][kSendPieces];
+#pragma unroll
+        for (int j = 0; j < kSlotGroup; ++j) {
+          const int r = j < D.k ? __builtin_amdgcn_readlane(row, j) : -1;
+#pragma unroll
+          for (int c = 0; c < kSendPieces; ++c) {
+            const int col = base + c * kWave * 8 + lane * 8;
+            v[j][c] = r >= 0 && col < D.H ? ld16(reinterpret_cast<const v4u*>(y + (int64_t)r * D.H + col))
+                                          : v4u{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < kSlotGroup; ++g) {
+          const int og = g < D.k ? __builtin_amdgcn_readlane(orow, g) : -1;
+          if (og < 0) continue;   // not a leader
+          const int dg = __builtin_amdgcn_readlane(dest, g);
+          float acc[kSendPieces][8];
+#pragma unroll
+          for (int c = 0; c < kSendPieces; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+#pragma unroll
+          for (int j = g; j < kSlotGroup; ++j) {
+            if (j >= D.k || __builtin_amdgcn_readlane(dest, j) != dg) continue;
+            const float wj = weight(j);
+#pragma unroll
+            for (int c = 0; c < kSendPieces; ++c) acc_row8(acc[c], wj, v[j][c]);
+          }
+#pragma unroll
+          for (int c = 0; c < kSendPieces; ++c) {
+            const int col = base + c * kWave * 8 + lane * 8;
+            if (col < D.H) st16(reinterpret_cast<v4u*>(comb + (int64_t)og * D.H + col), pack_bf16x8(acc[c]));
+          }
+        }
+      }
+    } else {
+      for (int g = 0; g < D.k; ++g) {
+        const int og = __builtin_amdgcn_readlane(orow, g);
+        if (og < 0) continue;
+        const int dg = __builtin_amdgcn_readlane(dest, g);
+        for (int base = 0; base < D.H; base += kWave * 8) {
+          const int col = base + lane * 8;
+          float acc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+          for (int j0 = g; j0 < D.k; j0 += kSlotGroup) {
+            v4u v[kSlotGroup];
+            int rr[kSlotGroup];
+#pragma unroll
+            for (int jj = 0; jj < kSlotGroup; ++jj) {
+              const int j = j0 + jj;
+              rr[jj] = j < D.k && __builtin_amdgcn_readlane(dest, j < D.k ? j : 0) == dg
+                           ? __builtin_amdgcn_readlane(row, j < D.k ? j : 0)
+                           : -1;
+              v[jj] = rr[jj] >= 0 && col < D.H
+                          ? ld16(reinterpret_cast<const v4u*>(y + (int64_t)rr[jj] * D.H + col))
+                          : v4u{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSlotGroup; ++jj)
+              if (rr[jj] >= 0) acc_row8(acc, weight(j0 + jj), v[jj]);
+          }
+          if (col < D.H) st16(reinterpret_cast<v4u*>(comb + (int64_t)og * D.H + col), pack_bf16x8(acc));
+        }
+      }
+    }
+  }
 }
 
 // Plain streaming copy: each workgroup copies one contiguous chunk.
@@ -211,6 +375,22 @@ int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* i
   if (D.N * D.T == 0) return MOE_OK;
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
   return launch("k_comb_pull", k_comb_pull, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
+}
+
+int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
+                             const float* w, uint16_t* comb, int cus, hipStream_t st) {
+  if (D.N * D.T == 0) return MOE_OK;
+  const int grid = stream_grid(kSendPartialShape, cus, (int64_t)D.N * D.T, kSpWaves);
+  return launch("k_comb_send_partial", k_comb_send_partial, dim3(grid), dim3(kSpThreads), 0, st, D, W, y, idx,
+                send_pos, w, comb);
+}
+
+int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
+                             uint16_t* out, int cus, hipStream_t st) {
+  if (D.N * D.T == 0) return MOE_OK;
+  const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
+  return launch("k_comb_recv_partial", k_comb_recv_partial, dim3(grid), dim3(kCrThreads), 0, st, D, W, comb, idx,
+                send_pos, out);
 }
 
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st) {

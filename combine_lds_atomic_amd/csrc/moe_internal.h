@@ -217,7 +217,11 @@ struct LaunchShape {
 constexpr LaunchShape kPackShape = MOE_PACK_SHAPE;
 constexpr LaunchShape kUnpackShape = MOE_UNPACK_SHAPE;
 constexpr LaunchShape kCombSendShape = MOE_COMB_SEND_SHAPE;
+#ifndef MOE_SEND_PARTIAL_SHAPE
+#define MOE_SEND_PARTIAL_SHAPE {16, 1}
+#endif
 constexpr LaunchShape kCombRecvShape = MOE_COMB_RECV_SHAPE;
+constexpr LaunchShape kSendPartialShape = MOE_SEND_PARTIAL_SHAPE;
 constexpr LaunchShape kCopyShape = {16, 1};
 
 // Grid of a streaming kernel of shape S over `items` work units, at most
@@ -292,6 +296,10 @@ int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* i
                      const float* w, uint16_t* out, int cus, hipStream_t st);
 int launch_dispatch_ll(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos,
                        uint8_t* recv_q, float* recv_s, int cus, hipStream_t st);
+int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
+                             const float* w, uint16_t* comb, int cus, hipStream_t st);
+int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
+                             uint16_t* out, int cus, hipStream_t st);
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 

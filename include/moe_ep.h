@@ -221,6 +221,40 @@ int moe_combine_pull(const moe_shape *shape, const uint16_t *y_em, const int32_t
                      const float *topk_w, const void *ws, uint16_t *out, void *stream);
 
 /*
+ * Combine with send-side partial accumulation, send half ("Evaluation:
+ * dispatch/combine latency": summing a token's rows on the send side of
+ * combine cuts the data sent, possibly at some cost in accuracy).  A group is
+ * the set of a token's slots whose expert-major rows sit on one rank; its
+ * leader is its first slot.  For every group of every token (s, t):
+ *   comb[s*T*k + send_pos[s][t][leader]] =
+ *       bf16_rne(sum over the group's slots j, in slot order, of w[s][t][j] * y_j),
+ * float32 accumulation with no fused multiply-add.  Rows of comb that no
+ * group leads are left untouched.  Slots without a row (bad id, or a row a
+ * full fixed region dropped) belong to no group.
+ *   y_em, topk_idx, send_pos, topk_w, ws   as for moe_combine_pull (the
+ *                                          weights travel with the tokens).
+ *   comb   bf16 [N][T*k][H] out, 16-B aligned.
+ */
+int moe_combine_send_partial(const moe_shape *shape, const uint16_t *y_em, const int32_t *topk_idx,
+                             const int32_t *send_pos, const float *topk_w, const void *ws, uint16_t *comb,
+                             void *stream);
+
+/*
+ * Combine with send-side partial accumulation, receive half:
+ *   out[s][t] = bf16_rne(sum over the token's groups, in leader order, of
+ *               the group row comb[s*T*k + send_pos[s][t][leader]]),
+ * float32 accumulation, no weights (the sender applied them).
+ *   comb      from moe_combine_send_partial.
+ *   topk_idx, send_pos, ws   as given to moe_combine_send_partial.
+ *   out       bf16 [N][T][H] out, 16-B aligned.
+ * It differs from moe_combine_recv by the rounding of each group sum to bf16:
+ * |out - sum_j w_j y_j| <= 2^-8 (|out| + sum_g |group row g|)
+ *                          + 2k 2^-24 sum_j |w_j y_j|.
+ */
+int moe_combine_recv_partial(const moe_shape *shape, const uint16_t *comb, const int32_t *topk_idx,
+                             const int32_t *send_pos, const void *ws, uint16_t *out, void *stream);
+
+/*
  * Wait for `stream`, return the sticky error bits accumulated in ws since the
  * last call (MOE_FLAG_*) through *flags, and clear them.  The only call that
  * blocks the host.

@@ -87,6 +87,12 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     assert lib.moe_combine_pull(s, _p(A), _p(A), _p(A), _p(A), None, _p(A), None) == -2     # no ws
     assert lib.moe_combine_pull(s, _p(A), None, _p(A), _p(A), _p(A), _p(A), None) == -2     # no ids
     assert lib.moe_combine_pull(s, _p(A + 8), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -3
+    assert lib.moe_combine_send_partial(s, _p(A), _p(A), _p(A), _p(A), None, _p(A), None) == -2   # no ws
+    assert lib.moe_combine_send_partial(s, _p(A), _p(A), _p(A), None, _p(A), _p(A), None) == -2   # no weights
+    assert lib.moe_combine_send_partial(s, _p(A), _p(A), _p(A), _p(A), _p(A), _p(A + 8), None) == -3
+    assert lib.moe_combine_recv_partial(s, _p(A), _p(A), _p(A), None, _p(A), None) == -2          # no ws
+    assert lib.moe_combine_recv_partial(s, _p(A), None, _p(A), _p(A), _p(A), None) == -2          # no ids
+    assert lib.moe_combine_recv_partial(s, _p(A), _p(A), _p(A), _p(A), _p(A + 2), None) == -3
     fl = ctypes.c_uint32()
     assert lib.moe_status(None, None, ctypes.byref(fl)) == -2
     assert lib.moe_status(_p(A + 4), None, ctypes.byref(fl)) == -3

@@ -1,0 +1,187 @@
+"""GPU parity of the combine with send-side partial accumulation
+(moe_combine_send_partial + moe_combine_recv_partial) against the oracle's
+combine_partial.
+
+Both halves are bit-exact against the oracle (the same float32 operations in
+the same order, one bf16 rounding per group row and one for the result):
+the group rows at their leaders' positions, the untouched rows of comb and
+the output.  The output also meets this mode's own tolerance against the
+exact sum, |out - sum_j w_j y_j| <= 2^-8 (|out| + sum_g |p_g|) +
+2k 2^-24 sum_j |w_j y_j|.  Small shapes compare every element; the full-size
+workloads compare every output token of a sample."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_lds_atomic_amd as moe
+import workloads as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import bf16_np, log, run_all  # noqa: E402
+
+FILL = 0x3F00
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    log(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _cfg(name, **kw):
+    return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
+
+
+def _partial(r):
+    """Run both halves on the buffers of a run_all result."""
+    sh, B = r["sh"], r["B"]
+    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).cuda()
+    w_d = torch.from_numpy(np.ascontiguousarray(r["w"], np.float32)).cuda()
+    comb = torch.empty_like(B.comb)
+    comb.view(torch.int16).fill_(FILL)
+    out = torch.full_like(B.out, 3.0)
+    moe.moe_combine_send_partial(sh, r["y"], idx_d, B.send_pos, w_d, B.ws, comb)
+    moe.moe_combine_recv_partial(sh, comb, idx_d, B.send_pos, B.ws, out)
+    assert moe.moe_status(B.ws) & moe.FLAG_TIMEOUT == 0
+    return comb, out
+
+
+def _bound_check(out_bits, rows_by_slot, w_tok, group_rows):
+    """The derived tolerance against the float64 sum, one token."""
+    o = O.bf16_from_bits(out_bits).astype(np.float64)
+    ww = np.asarray(w_tok, np.float64)[:, None]
+    exact = (ww * rows_by_slot).sum(axis=0)
+    mag = (np.abs(ww) * np.abs(rows_by_slot)).sum(axis=0)
+    pg = sum(np.abs(O.bf16_from_bits(p).astype(np.float64)) for p in group_rows) if group_rows else 0.0
+    k = len(w_tok)
+    lim = 2.0 ** -8 * (np.abs(o) + pg) + 2 * k * 2.0 ** -24 * mag + 2.0 ** -133
+    assert (np.abs(o - exact) <= lim).all()
+
+
+def _full_check(r, region_rows=0):
+    sh = r["sh"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    lay = O.layout(r["idx"], sh.E, N, region_rows)
+    comb, out = _partial(r)
+    y = bf16_np(r["y"])
+    comb_o, lead, out_o = O.combine_partial(y, r["idx"], lay, r["w"])
+    got_comb = bf16_np(comb).reshape(N * T * k, H)
+    led = np.zeros(N * T * k, bool)
+    for s in range(N):
+        for t in range(T):
+            for j in np.flatnonzero(lead[s, t]):
+                led[s * T * k + lay.send_pos[s, t, j]] = True
+    assert (got_comb[led] == comb_o[led]).all(), "group rows"
+    assert (got_comb[~led] == FILL).all(), "rows no group leads were written"
+    got_out = bf16_np(out)
+    assert (got_out == out_o).all(), f"out differs at {np.count_nonzero(got_out != out_o)} elements"
+    yv = O.bf16_from_bits(y).astype(np.float64)
+    for s in range(N):
+        for t in range(T):
+            part = lay.em_row[s, t] >= 0
+            rows = np.zeros((k, H))
+            rows[part] = yv[lay.em_row[s, t][part]]
+            grp = [comb_o[s * T * k + lay.send_pos[s, t, j]] for j in np.flatnonzero(lead[s, t])]
+            _bound_check(got_out[s, t], rows, np.where(part, r["w"][s, t], 0.0), grp)
+    return lay, lead
+
+
+def test_tiny_config():
+    _full_check(run_all(W.CONFIGS["tiny"], 128))
+
+
+@pytest.mark.parametrize("N,T,H,E,k", [
+    (8, 33, 256, 16, 8),        # k = E/N: tokens often keep two slots on one rank
+    (5, 77, 9216, 40, 6),       # rows longer than 8 columns per lane, ragged
+    (4, 20, 256, 64, 12),       # k > 8: groups taken one after another
+    (2, 5, 128, 4, 1),          # one slot per token
+    (16, 9, 384, 16, 4),        # one expert per rank: every slot its own group
+    (3, 1500, 384, 12, 3),      # many tokens, ragged workgroup ranges
+])
+def test_shapes(N, T, H, E, k):
+    _full_check(run_all(_cfg(f"cp{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k), T))
+
+
+def test_all_slots_on_one_rank_equals_plain_combine():
+    cfg = _cfg("cp_forced", N=8, T=200, H=256, E=64, k=8, forced_rank0=True)
+    r = run_all(cfg, 200)
+    _, lead = _full_check(r)
+    assert (lead.sum(axis=2) == 1).all()
+    _, out = _partial(r)
+    assert torch.equal(out.view(torch.int16), r["B"].out.view(torch.int16))
+
+
+def test_bad_ids():
+    cfg = _cfg("cp_badid", N=4, T=40, H=256, E=16, k=4)
+    idx, w = W.routing(cfg, 40)
+    idx = idx.copy()
+    idx[0, 3, 1] = 16
+    idx[2, 7, 0] = -1
+    idx[3, 39, 3] = 1 << 30
+    _full_check(run_all(cfg, 40, idx=idx, w=w))
+
+
+def test_fixed_region_overflow():
+    cfg = _cfg("cp_ovf", N=4, T=64, H=256, E=8, k=3)
+    idx, w = W.routing(cfg, 64)
+    idx = idx.copy()
+    idx[:, :, 0] = 0
+    R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) - 9
+    r = run_all(cfg, 64, R, idx=idx, w=w)
+    assert r["flags"] & O.FLAG_OVERFLOW
+    _full_check(r, R)
+
+
+def _sampled(r, n_tok=40, seed=3):
+    sh, B = r["sh"], r["B"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    lay = O.layout(r["idx"], sh.E, N)
+    comb, out = _partial(r)
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([rng.choice(N * T, n_tok, replace=False), [0, N * T - 1]]))
+    dev = B.ws.device
+    L = sh.E // N
+    for tk in toks:
+        s, t = divmod(int(tk), T)
+        part = lay.em_row[s, t] >= 0
+        em = np.where(part, lay.em_row[s, t], 0)
+        rows = bf16_np(r["y"][torch.from_numpy(em).to(dev)])
+        rows[~part] = 0
+        dest = np.where(lay.slot_valid[s, t], r["idx"][s, t], 0) // L
+        groups, want = O.partial_token(rows, r["w"][s, t], dest, part)
+        for j, p in groups:
+            got = bf16_np(comb[s, lay.send_pos[s, t, j]])
+            assert (got == p).all(), (s, t, j)
+        got_out = bf16_np(out[s, t])
+        assert (got_out == want).all(), (s, t)
+        _bound_check(got_out, O.bf16_from_bits(rows).astype(np.float64), np.where(part, r["w"][s, t], 0.0),
+                     [p for _, p in groups])
+
+
+def _need(gib):
+    free, _ = torch.cuda.mem_get_info()
+    if free < gib * 2 ** 30:
+        pytest.skip(f"needs {gib} GiB of free device memory, {free / 2**30:.0f} GiB free")
+
+
+def test_combine_heavy_full_size():
+    _need(45)
+    cfg = W.CONFIGS["combine_heavy"]
+    _sampled(run_all(cfg, cfg.T, fill=None))
+
+
+def test_dsv3_decode_full_size():
+    cfg = W.CONFIGS["dsv3_decode"]
+    _sampled(run_all(cfg, cfg.T, fill=None))
+
+
+def test_kimi_combine_full_size():
+    _need(100)
+    cfg = W.CONFIGS["kimi_skewed"]
+    _sampled(run_all(cfg, cfg.Tc, payload=False, fill=None))
