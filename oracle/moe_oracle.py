@@ -190,10 +190,12 @@ class Layout:
     k: int
     L: int
     region_rows: int            # 0 = packed regions, R > 0 = region d at rows [d*R, d*R + R)
+    early_rows: int             # C: private rows per sender at the start of every fixed region (0 = none)
     cnt: np.ndarray             # [N, E]  tokens of source s routed to expert e
     send_off: np.ndarray        # [N, E+1] exclusive scan of cnt[s] over experts
     send_pos: np.ndarray        # [N, T, k] position of each slot in its sender's order; -1 = dropped
-    recv_off: np.ndarray        # [N(d), N(s)+1] start of source s's block inside region d
+    recv_off: np.ndarray        # [N(d), N(s)+1] start of source s's block inside region d (of its rows beyond
+                                #                the early rows, counted from row N*C, when C > 0)
     recv_total: np.ndarray      # [N]     rows destined to region d
     base: np.ndarray            # [N+1]   first physical row of region d (base[N] = rows in use / allocated)
     exp_off: np.ndarray         # [N(d), L+1] expert offsets inside region d (grouped-GEMM layout)
@@ -209,13 +211,24 @@ class Layout:
         return self.N * self.T * self.k if self.region_rows == 0 else self.N * self.region_rows
 
 
-def layout(idx, E: int, N: int, region_rows: int = 0) -> Layout:
+def layout(idx, E: int, N: int, region_rows: int = 0, early_rows: int = 0) -> Layout:
     """Everything dispatch decides from the routing alone.
 
     idx: int [N, T, k] expert chosen by slot j of token t on source rank s.
+    early_rows: C > 0 reserves, at the start of every fixed region, C private
+    rows per sender ([EFA] "Send and receive buffers": a little private
+    per-sender space on every receiver lets some tokens go out with the
+    routing information, before the exchange).  Reading: sender s's first C
+    rows for region d (in its sender order) go to rows s*C .. s*C + C - 1 of
+    the region, a place the sender knows without the exchange; its further
+    rows follow from row N*C, stacked by source as without early rows.  Only
+    with fixed regions (a packed region's start depends on the exchange), and
+    N*C <= R.
     """
     idx = np.asarray(idx, dtype=np.int64)
     assert idx.ndim == 3 and idx.shape[0] == N
+    C = early_rows
+    assert C == 0 or (region_rows > 0 and N * C <= region_rows)
     _, T, k = idx.shape
     assert E % N == 0
     L = E // N
@@ -246,11 +259,13 @@ def layout(idx, E: int, N: int, region_rows: int = 0) -> Layout:
         sp = send_pos[s].reshape(-1)
         sp[order] = np.arange(order.size)
 
-    # O5 receive regions: c[s, d] rows go from s to d, stacked by source.
+    # O5 receive regions: c[s, d] rows go from s to d, stacked by source (with
+    # early rows: only the rows beyond each sender's first C).
     c = np.add.reduceat(cnt, np.arange(0, E, L), axis=1) if E > 0 else cnt   # [N(s), N(d)]
+    over = np.maximum(c - C, 0)
     recv_off = np.zeros((N, N + 1), np.int64)
-    recv_off[:, 1:] = np.cumsum(c.T, axis=1)            # scan over sources, per destination
-    recv_total = recv_off[:, N].copy()
+    recv_off[:, 1:] = np.cumsum(over.T, axis=1)         # scan over sources, per destination
+    recv_total = c.sum(axis=0)
     bound = N * T * max(k, L)
     if (recv_total > bound).any():
         flags |= FLAG_BOUND
@@ -274,7 +289,8 @@ def layout(idx, E: int, N: int, region_rows: int = 0) -> Layout:
     s_of = np.broadcast_to(np.arange(N)[:, None, None], idx.shape)
     d = e // L
     l = e - d * L
-    in_region = recv_off[d, s_of] + (send_pos - send_off[s_of, d * L])
+    u = send_pos - send_off[s_of, d * L]                # index inside the (source, destination) block
+    in_region = np.where(u < C, s_of * C + u, N * C + recv_off[d, s_of] + (u - C))
     in_em = exp_off[d, l] + src_in_exp[s_of, e] + (send_pos - send_off[s_of, e])
     # A fixed region keeps the rows that fit it: a source-major row exists if
     # its region row is below R; an expert-major row exists if its own index
@@ -289,7 +305,7 @@ def layout(idx, E: int, N: int, region_rows: int = 0) -> Layout:
     recv_row = np.where(recv_fits, base[d] + in_region, -1)
     em_row = np.where(em_fits, base[d] + in_em, -1)
 
-    return Layout(N=N, T=T, E=E, k=k, L=L, region_rows=region_rows, cnt=cnt,
+    return Layout(N=N, T=T, E=E, k=k, L=L, region_rows=region_rows, early_rows=C, cnt=cnt,
                   send_off=send_off, send_pos=send_pos, recv_off=recv_off,
                   recv_total=recv_total, base=base, exp_off=exp_off,
                   src_in_exp=src_in_exp, slot_valid=valid, recv_row=recv_row,

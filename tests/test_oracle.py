@@ -162,6 +162,62 @@ def test_layout_golden_packed_and_fixed():
     assert (np.delete(rs, g["fixed_R8"]["row_src_rows"]) == -1).all()
 
 
+def test_layout_golden_early_rows():
+    g = _load("layout_tiny.json")
+    idx = np.array(g["idx"])
+    ex = g["fixed_R8_early2"]
+    lay = O.layout(idx, g["E"], g["N"], 8, 2)
+    assert lay.flags == 0
+    assert (lay.recv_off == ex["recv_off"]).all()
+    assert (lay.recv_total == g["recv_total"]).all()
+    got = {}
+    for s in range(2):
+        for t in range(g["T"]):
+            for j in range(2):
+                got[str(int(lay.recv_row[s, t, j]))] = [s, t]
+    assert got == ex["recv_row_token"]
+    rs = O.row_src(lay)
+    assert (rs[ex["row_src_rows"]] == ex["row_src"]).all()
+    assert (np.delete(rs, ex["row_src_rows"]) == -1).all()
+    ov = O.layout(idx, g["E"], g["N"], 5, 2)
+    assert ov.flags == g["fixed_R5_early2_overflow"]["flags"]
+    for s, t, j in g["fixed_R5_early2_overflow"]["dropped_slots"]:
+        assert ov.recv_row[s, t, j] == -1
+    assert (ov.recv_row >= 0).sum() == 10
+
+
+@pytest.mark.parametrize("N,T,E,k,C,seed", [(4, 40, 16, 4, 3, 1), (3, 25, 6, 2, 1, 2), (5, 30, 20, 3, 0, 3),
+                                            (2, 64, 8, 8, 40, 4)])
+def test_layout_early_rows_closed_form(N, T, E, k, C, seed):
+    """Region d's source-major rows are, for each sender s, its first
+    min(c[s,d], C) rows at s*C.. in sender order, then its remaining rows in
+    one run from N*C + (remaining rows of earlier senders); the expert-major
+    rows do not depend on C."""
+    rng = np.random.default_rng(seed)
+    idx = _random_idx(rng, N, T, E, k)
+    base = O.layout(idx, E, N)
+    R = N * C + int(base.recv_total.max()) + 3
+    lay = O.layout(idx, E, N, R, C)
+    ref = O.layout(idx, E, N, R)
+    assert lay.flags == 0
+    assert (lay.em_row == ref.em_row).all() and (O.row_src(lay) == O.row_src(ref)).all()
+    L = E // N
+    c = np.zeros((N, N), np.int64)
+    for s in range(N):
+        for e in idx[s].reshape(-1):
+            c[s, e // L] += 1
+    for d in range(N):
+        prior = 0
+        for s in range(N):
+            mine = [(int(lay.send_pos[s, t, j]), int(lay.recv_row[s, t, j]))
+                    for t in range(T) for j in range(k) if idx[s, t, j] // L == d]
+            rows = [r - d * R for _, r in sorted(mine)]          # in sender order
+            m = min(c[s, d], C)
+            assert rows[:m] == list(range(s * C, s * C + m))
+            assert rows[m:] == list(range(N * C + prior, N * C + prior + c[s, d] - m))
+            prior += c[s, d] - m
+
+
 def _brute_layout(idx, E, N):
     """Independent dict-of-lists construction of the same layout."""
     _, T, k = idx.shape
