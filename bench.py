@@ -248,6 +248,48 @@ def main():
         single_ms = ms_l.mean(axis=0)[0]
         single_p90 = np.percentile(ms_l[:, 0], 90)
 
+        # The same with early rows: fixed regions that start with C private
+        # rows per sender (C about 1.25x the mean rows of a rank pair), so
+        # most packers need only their own rank's count.  Regions are sized
+        # from the routing to hold everything.
+        L = cfg.E // cfg.N
+        C = max(1, int(np.ceil(1.25 * T * cfg.k / cfg.N)))
+        pair = np.zeros((cfg.N, cfg.N), np.int64)
+        for s_ in range(cfg.N):
+            pair[s_] = np.bincount(idx[s_].reshape(-1) // L, minlength=cfg.N)
+        R = int(cfg.N * C + np.maximum(pair - C, 0).sum(axis=0).max())
+        she = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, R, C)
+        Be = moe.allocate(she, dev, combine=False)
+        ye = W.expert_outputs(cfg, Be.rows, dev)
+        comb_e = torch.empty((cfg.N, T * cfg.k, cfg.H), dtype=torch.bfloat16, device=dev)
+        out_e = torch.empty((cfg.N, T, cfg.H), dtype=torch.bfloat16, device=dev)
+        w_d = torch.from_numpy(w).to(dev)       # weights of the dispatch batch
+
+        def step_e(ev=None):
+            if ev: ev[0].record(stream)
+            moe.moe_dispatch_send_ll(she, x, idx_d, Be.recv_q, Be.recv_s, Be.send_pos, Be.ws)
+            if ev: ev[1].record(stream)
+            moe.moe_dispatch_recv(she, Be.recv_q, Be.recv_s, Be.ws, Be.x_q, Be.x_s, Be.exp_off, Be.row_src)
+            if ev: ev[2].record(stream)
+            moe.moe_combine_send(she, ye, Be.row_src, Be.ws, comb_e)
+            if ev: ev[3].record(stream)
+            moe.moe_combine_recv(she, comb_e, Be.send_pos, w_d, out_e)
+            if ev: ev[4].record(stream)
+
+        for _ in range(args.warmup):
+            step_e()
+        eve = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step_e(eve[i])
+        torch.cuda.synchronize()
+        ms_e = np.array([[eve[i][p].elapsed_time(eve[i][p + 1]) for p in range(4)] for i in range(args.steps)])
+        same_e = bool(torch.equal(Be.send_pos, B.send_pos))
+        early_ms = ms_e.mean(axis=0)[0]
+        single["early_rows"] = {"early_rows": C, "region_rows": R, "dispatch_send": None,
+                                "same_send_pos": same_e}
+        del Be, ye, comb_e, out_e
+
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(2):
@@ -311,6 +353,7 @@ def main():
     phase_info = {name: info(name, per_phase_ms[p], p90_ms[p]) for p, name in enumerate(PHASES)}
     if single is not None:
         single["dispatch_send"] = info("dispatch_send", single_ms, single_p90)
+        single["early_rows"]["dispatch_send"] = info("dispatch_send", early_ms)
     dom_name = PHASES[dom]
     achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
     kernel = KERNEL_OF[dom_name]

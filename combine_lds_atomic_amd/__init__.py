@@ -28,15 +28,15 @@ class MoeError(RuntimeError):
 
 class moe_shape(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("k", ctypes.c_int32), ("reserved", ctypes.c_int32), ("region_rows", ctypes.c_int64)]
+                ("k", ctypes.c_int32), ("early_rows", ctypes.c_int32), ("region_rows", ctypes.c_int64)]
 
     def __repr__(self):
         return (f"moe_shape(N={self.N}, T={self.T}, H={self.H}, E={self.E}, k={self.k}, "
-                f"region_rows={self.region_rows})")
+                f"region_rows={self.region_rows}, early_rows={self.early_rows})")
 
 
-def shape(N: int, T: int, H: int, E: int, k: int, region_rows: int = 0) -> moe_shape:
-    return moe_shape(N, T, H, E, k, 0, region_rows)
+def shape(N: int, T: int, H: int, E: int, k: int, region_rows: int = 0, early_rows: int = 0) -> moe_shape:
+    return moe_shape(N, T, H, E, k, early_rows, region_rows)
 
 
 if not os.path.exists(LIB_PATH):

@@ -22,7 +22,8 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 int make_dims(const moe_shape* sh, Dims* D) {
   if (!sh) return MOE_ENULL;
   const moe_shape& s = *sh;
-  if (s.reserved != 0) return MOE_EINVAL;
+  if (s.early_rows < 0) return MOE_EINVAL;
+  if (s.early_rows > 0 && (s.region_rows == 0 || (int64_t)s.N * s.early_rows > s.region_rows)) return MOE_EINVAL;
   if (s.N < 1 || s.N > kMaxN) return MOE_EINVAL;
   if (s.T < 0) return MOE_EINVAL;
   if (s.H < kScaleBlock || s.H > kMaxH || s.H % kScaleBlock) return MOE_EINVAL;
@@ -54,6 +55,7 @@ int make_dims(const moe_shape* sh, Dims* D) {
   D->B = (int)((tk + C - 1) / C);
   D->NB = s.H / kScaleBlock;
   D->R = (int)s.region_rows;
+  D->Ce = s.early_rows;
   D->rows = (int)rows;
   D->bound = (int64_t)s.N * s.T * (s.k > D->L ? s.k : D->L);
   return MOE_OK;
@@ -94,6 +96,7 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->trel = take64((size_t)D.N * D.N);
   W->tbase = take64((size_t)D.N);
   W->tready = take64((size_t)kReadyCopies * kReadyStride);
+  W->tcdone = take64((size_t)D.N * kReadyStride);
   return o;
 }
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ int em_row_of(const Dims& D, const Ws& W, int s, int 
   const int* so = W.send_off + s * (D.E + 1);
   const int u = sp - so[e];                                                         // index inside (s, e)
   const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;      // expert-major
-  const int j = W.recv_off[d * (D.N + 1) + s] + (so[e] - so[d * D.L]) + u;         // source-major
+  const int j = region_row(D, s, (so[e] - so[d * D.L]) + u, W.recv_off[d * (D.N + 1) + s]);   // source-major
   const int p = W.base[d] + i;
   return (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) ? p : -1;
 }
@@ -340,11 +340,15 @@ __global__ __launch_bounds__(kSpThreads) void k_comb_send_partial(Dims D, Ws W, 
   }
 }
 
-// Plain streaming copy: each workgroup copies one contiguous chunk.
+// Plain streaming copy: each workgroup copies one contiguous chunk, every
+// lane with kCopyUnroll loads in flight (8 measured ~3% faster than 4 on a
+// 1 GiB copy, the fastest pattern found: the ceiling the row kernels are
+// compared with).
+constexpr int kCopyUnroll = 8;
 __global__ __launch_bounds__(kCpThreads) void k_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src,
                                                         int64_t n) {
   const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  constexpr int U = 4;
+  constexpr int U = kCopyUnroll;
   int64_t i = b0 + threadIdx.x;
   for (; i + (U - 1) * kCpThreads < b1; i += U * kCpThreads) {
     v4u r[U];
@@ -395,7 +399,7 @@ int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, c
 
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st) {
   if (n16 == 0) return MOE_OK;
-  const int grid = stream_grid(kCopyShape, cus, n16, (int64_t)kCpThreads * 4);
+  const int grid = stream_grid(kCopyShape, cus, n16, (int64_t)kCpThreads * kCopyUnroll);
   return launch("k_copy16", k_copy16, dim3(grid), dim3(kCpThreads), 0, st, reinterpret_cast<v4u*>(dst),
                 reinterpret_cast<const v4u*>(src), n16);
 }

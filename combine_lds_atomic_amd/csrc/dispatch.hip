@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
           sp = send_pos[slot];
         }
         const int d = e / D.L;
-        const int r = W.recv_off[d * (D.N + 1) + s] + sp - W.send_off[s * (D.E + 1) + d * D.L];
+        const int r = region_row(D, s, sp - W.send_off[s * (D.E + 1) + d * D.L], W.recv_off[d * (D.N + 1) + s]);
         const int pr = W.base[d] + r;
         if ((D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
       }
@@ -272,14 +272,15 @@ __device__ __forceinline__ bool tag_wait3(const uint64_t* p0, const uint64_t* p1
 constexpr int kCrossBatch = 4;
 
 // LDS bytes of the cross-rank role.
-inline size_t cross_ll_lds_bytes(int E) { return sizeof(int) * ((size_t)kThreads + E + 1); }
+inline size_t cross_ll_lds_bytes(int E) { return sizeof(int) * ((size_t)2 * kThreads + E + 1); }
 
 // The cross-rank role: the same tables k_route_cross computes, from the
 // tagged send offsets and counts of the count workgroups.
 __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int* wsum) {
   const int N = D.N, E = D.E, L = D.L, tid = threadIdx.x;
-  int* part = sm;              // [G][N], G*N <= kThreads
-  int* ex = sm + kThreads;     // [E+1]
+  int* part = sm;                  // [G][N], G*N <= kThreads: rows beyond the early ones
+  int* partc = sm + kThreads;      // [G][N]: all rows
+  int* ex = sm + 2 * kThreads;     // [E+1]
   bool ok = true;
 
   // (1) rows from source s to destination d are
@@ -295,7 +296,7 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
   int lo1[kCrossBatch] = {}, hi1[kCrossBatch] = {};
   const bool one = s1 - s0 <= kCrossBatch;
   if (mine) {
-    int sum = 0;
+    int sum = 0, over = 0;
     for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
       const int n = min(kCrossBatch, s1 - sb);
       int lo[kCrossBatch] = {}, hi[kCrossBatch] = {};
@@ -303,22 +304,25 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
 #pragma unroll
       for (int u = 0; u < kCrossBatch; ++u) {
         sum += hi[u] - lo[u];
+        over += max(hi[u] - lo[u] - D.Ce, 0);
         lo1[u] = lo[u];
         hi1[u] = hi[u];
       }
     }
-    part[g * N + d] = sum;
+    part[g * N + d] = over;
+    partc[g * N + d] = sum;
   }
   __syncthreads();
-  int rt = 0;   // rows received by rank tid
+  int rt = 0, rover = 0;   // rows received by rank tid; of those, beyond the senders' early rows
   if (tid < N) {
     int a = 0;
     for (int g2 = 0; g2 < G; ++g2) {
       const int c = part[g2 * N + tid];
       part[g2 * N + tid] = a;
       a += c;
+      rt += partc[g2 * N + tid];
     }
-    rt = a;
+    rover = a;
   }
   // (2) Region bases, rows written per region, capacity and bound checks.
   int all, vall;
@@ -330,9 +334,9 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
     W.base[tid] = bd;
     W.vprefix[tid] = vb;
     W.recv_total[tid] = rt;
-    W.recv_off[tid * (N + 1) + N] = rt;
+    W.recv_off[tid * (N + 1) + N] = rover;
     uint32_t fl = 0;
-    if (D.R && rt > D.R) fl |= MOE_FLAG_OVERFLOW;
+    if (D.R && (rt > D.R || D.N * D.Ce + rover > D.R)) fl |= MOE_FLAG_OVERFLOW;
     if ((int64_t)rt > D.bound) fl |= MOE_FLAG_BOUND;
     if (fl) atomicOr(W.err, fl);
   }
@@ -341,7 +345,8 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
     W.vprefix[N] = vall;
   }
   // (3) recv_off[d][s], and what a packer of source s adds to a sender
-  // position to get its row inside region d: recv_off[d][s] - send_off[s][dL].
+  // position to get its row inside region d when the row is not one of the
+  // sender's early rows: N*Ce + recv_off[d][s] - Ce - send_off[s][dL].
   if (mine && ok) {
     int acc = part[g * N + d];
     for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
@@ -357,8 +362,8 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
       for (int u = 0; u < n && ok; ++u) {
         const int s = sb + u;
         W.recv_off[d * (N + 1) + s] = acc;
-        tag_put(W.trel + (int64_t)s * N + d, tag, acc - lo[u]);
-        acc += hi[u] - lo[u];
+        tag_put(W.trel + (int64_t)s * N + d, tag, N * D.Ce + acc - D.Ce - lo[u]);
+        acc += max(hi[u] - lo[u] - D.Ce, 0);
       }
     }
   }
@@ -428,6 +433,8 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
 
   if (wg < D.N) {
     count_chunk(D, W, idx, send_pos, wg, 0, smem, wsum, tag);
+    __syncthreads();
+    if (threadIdx.x == 0) tag_put(W.tcdone + wg * kReadyStride, tag, 1);
   } else if (wg == D.N) {
     cross_ll(D, W, tag, reinterpret_cast<int*>(smem), wsum);
   } else {
@@ -435,10 +442,21 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
     const int items = D.N * D.T * D.slices;
     const int lo = (int)((int64_t)items * p / npack), hi = (int)((int64_t)items * (p + 1) / npack);
     bool fail = false;
+    // Without early rows every packer needs the cross-rank results: wait
+    // for a "ready" copy.  With early rows it needs only its own source
+    // ranks' counts for most rows: wait for those ranks' count workgroups.
     auto gate = [&] {
-      if (threadIdx.x == 0) {
+      if (threadIdx.x == 0 && lo < hi) {
         int one;
-        if (!tag_wait(W.tready + (p % kReadyCopies) * kReadyStride, tag, &one)) {
+        bool ok;
+        if (D.Ce == 0) {
+          ok = tag_wait(W.tready + (p % kReadyCopies) * kReadyStride, tag, &one);
+        } else {
+          const int s_first = lo / D.slices / D.T, s_last = (hi - 1) / D.slices / D.T;
+          ok = tag_wait(W.tcdone + s_first * kReadyStride, tag, &one) &&
+               tag_wait(W.tcdone + s_last * kReadyStride, tag, &one);
+        }
+        if (!ok) {
           sh_fail = 1;
           atomicOr(W.err, MOE_FLAG_TIMEOUT);
         }
@@ -464,9 +482,22 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
         const int64_t slot = (int64_t)tok * D.k + lane;
         if (e >= 0 && e < D.E) {
           const int d = e / D.L;
-          int sp = 0, rel = 0, bd = D.R ? d * D.R : 0;
-          ok = tag_wait3(W.tpos + slot, W.trel + (int64_t)s * D.N + d, D.R ? nullptr : W.tbase + d, tag, sp, rel, bd);
-          const int r = rel + sp;
+          int sp = 0, rel = 0, bd = D.R ? d * D.R : 0, r = -1;
+          if (D.Ce == 0) {
+            ok = tag_wait3(W.tpos + slot, W.trel + (int64_t)s * D.N + d, D.R ? nullptr : W.tbase + d, tag, sp, rel,
+                           bd);
+            r = rel + sp;
+          } else {   // fixed regions: an early row needs only the sender's own count
+            int so = 0;
+            ok = tag_wait3(W.tpos + slot, W.toff + (int64_t)s * (D.N + 1) + d, nullptr, tag, sp, so, bd);
+            const int u = sp - so;
+            if (ok && u < D.Ce) {
+              r = s * D.Ce + u;
+            } else if (ok) {
+              ok = tag_wait(W.trel + (int64_t)s * D.N + d, tag, &rel);
+              r = rel + sp;
+            }
+          }
           const int pr = bd + r;
           if (ok && (D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
         }
@@ -549,7 +580,7 @@ __global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8
       const int s = min(floor_index(W.src_in_exp + e, N + 1, u1, E), N - 1);
       const int u = u1 - W.src_in_exp[s * E + e];
       const int* so = W.send_off + s * (E + 1);
-      const int j = W.recv_off[d * (N + 1) + s] + (so[e] - so[d * L]) + u;   // source-major row
+      const int j = region_row(D, s, (so[e] - so[d * L]) + u, W.recv_off[d * (N + 1) + s]);   // source-major row
       const int pd = W.base[d] + i;
       if (pd < D.rows) {
         dst = pd;

@@ -117,7 +117,8 @@ constexpr int kCrossMaxN = 128;
 __global__ __launch_bounds__(kScanThreads) void k_route_cross(Dims D, Ws W) {
   __shared__ int tab[kCrossTable];
   __shared__ int ex[kMaxE + 1];
-  __shared__ int rt[kMaxN];
+  __shared__ int rt[kMaxN];   // rows each destination receives
+  __shared__ int ro[kMaxN];   // of those, rows beyond the senders' early rows
   __shared__ int wsum[kScanWaves + 1];
   const int tid = threadIdx.x;
   const int N = D.N, E = D.E, L = D.L;
@@ -170,16 +171,20 @@ __global__ __launch_bounds__(kScanThreads) void k_route_cross(Dims D, Ws W) {
       if (i < N * N) tab[i] = cv[u];
     }
     __syncthreads();
-    // (3b) recv_off[d][s] = rows from sources before s, stacked by source.
+    // (3b) recv_off[d][s] = rows from sources before s, stacked by source
+    // (with early rows: only each source's rows beyond its first Ce).
     for (int d = tid; d < N; d += kScanThreads) {
-      int acc = 0;
+      int acc = 0, tot = 0;
       for (int s = 0; s < N; ++s) {
+        const int c = tab[s * N + d];
         W.recv_off[d * (N + 1) + s] = acc;
-        acc += tab[s * N + d];
+        acc += max(c - D.Ce, 0);
+        tot += c;
       }
       W.recv_off[d * (N + 1) + N] = acc;
-      W.recv_total[d] = acc;
-      rt[d] = acc;
+      W.recv_total[d] = tot;
+      rt[d] = tot;
+      ro[d] = acc;
     }
     __syncthreads();
   } else {
@@ -218,26 +223,33 @@ __global__ __launch_bounds__(kScanThreads) void k_route_cross(Dims D, Ws W) {
       const int per = (N + G - 1) / G;
       const int s0 = min(N, g * per), s1 = min(N, s0 + per);
       const int* so_all = W.send_off;
-      auto get = [&](int s2) {
+      auto getc = [&](int s2) {
         const int* o = so_all + s2 * (E + 1);
         return o[(d + 1) * L] - o[d * L];
       };
-      if (mine) part[g * N + d] = sum_range(s0, s1, get);
+      auto get = [&](int s2) { return max(getc(s2) - D.Ce, 0); };   // rows beyond the early ones
+      int* partc = part + kScanThreads;
+      if (mine) {
+        part[g * N + d] = sum_range(s0, s1, get);
+        partc[g * N + d] = sum_range(s0, s1, getc);
+      }
       __syncthreads();
       for (int d2 = tid; d2 < N; d2 += kScanThreads) {
-        int a = 0;
+        int a = 0, b = 0;
         for (int g2 = 0; g2 < G; ++g2) {
           const int c = part[g2 * N + d2];
           part[g2 * N + d2] = a;
           a += c;
+          b += partc[g2 * N + d2];
         }
         W.recv_off[d2 * (N + 1) + N] = a;
-        W.recv_total[d2] = a;
-        rt[d2] = a;
+        W.recv_total[d2] = b;
+        rt[d2] = b;
+        ro[d2] = a;
       }
       __syncthreads();
-      int* ro = W.recv_off + d * (N + 1);
-      if (mine) scan_range(s0, s1, part[g * N + d], get, [&](int s2, int v) { ro[s2] = v; });
+      int* rof = W.recv_off + d * (N + 1);
+      if (mine) scan_range(s0, s1, part[g * N + d], get, [&](int s2, int v) { rof[s2] = v; });
       __syncthreads();
     }
   }
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(kScanThreads) void k_route_cross(Dims D, Ws W) {
       W.base[tid] = D.R ? tid * D.R : b;
       W.vprefix[tid] = vb;
       uint32_t fl = 0;
-      if (D.R && r > D.R) fl |= MOE_FLAG_OVERFLOW;
+      if (D.R && (r > D.R || D.N * D.Ce + ro[tid] > D.R)) fl |= MOE_FLAG_OVERFLOW;
       if ((int64_t)r > D.bound) fl |= MOE_FLAG_BOUND;
       if (fl) atomicOr(W.err, fl);
     }

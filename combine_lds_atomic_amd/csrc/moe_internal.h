@@ -59,6 +59,7 @@ struct Dims {
   int NB;       // scale blocks per row = H/128
   int slices;   // pack work items per token (1 = whole row per wave)
   int R;        // fixed region rows, 0 = packed
+  int Ce;       // early (private) rows per sender in each fixed region, 0 = none
   int rows;     // rows of every receive / expert-major array
   int64_t bound;  // N*T*max(k, L)
 };
@@ -89,6 +90,7 @@ struct Ws {
   uint64_t *trel;     // [N][N] recv_off[d][s] - send_off[s][d*L]
   uint64_t *tbase;    // [N] region bases
   uint64_t *tready;   // [kReadyCopies][kReadyStride]: published after the values packers need
+  uint64_t *tcdone;   // [N][kReadyStride]: rank s's count work is published (early rows)
 };
 
 // Copies of the "ready" word, one per 64-byte line, so that the waiting
@@ -181,6 +183,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float q) {
   // moves into the exponent.  Rebias 127 -> 7.
   const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
   return sign | (r - (120u << 3));
+}
+
+// Row inside region d of block index u of source s's rows for d (u =
+// send_pos - send_off[s][d*L]), given recv_off[d][s]: the sender's early
+// rows first, then its share of the region's common part.
+__device__ __forceinline__ int region_row(const Dims& D, int s, int u, int recv_off_ds) {
+  return u < D.Ce ? s * D.Ce + u : D.N * D.Ce + recv_off_ds + (u - D.Ce);
 }
 
 // ------------------------------------------------------------------ streaming rows

@@ -84,11 +84,19 @@ extern "C" {
  *                and the arrays hold N*R rows.  R = N*T*max(k, E/N) is the
  *                worst-case bound of "Send and receive buffers" and never
  *                overflows.
+ *   early_rows   C > 0 (fixed regions only, N*C <= R): region d starts with
+ *                C private rows per sender ("Send and receive buffers": a
+ *                little private per-sender space on every receiver lets
+ *                some tokens go out before the count exchange).  Sender s's
+ *                first C rows for d go to region rows s*C .. s*C + C - 1 in
+ *                its sender order, a place it knows without the exchange;
+ *                its further rows follow from region row N*C, stacked by
+ *                source.  The expert-major layout does not change.
  * N*T*k and N*R must stay below 2^31.
  */
 typedef struct moe_shape {
   int32_t N, T, H, E, k;
-  int32_t reserved; /* must be 0 */
+  int32_t early_rows; /* C: private rows per sender in every fixed region, 0 = none */
   int64_t region_rows;
 } moe_shape;
 
@@ -118,8 +126,10 @@ int moe_workspace_init(const moe_shape *shape, void *ws, void *stream);
  *   topk_idx  int32 [N][T][k]: expert of slot j of token t on rank s.
  *   recv_q    fp8 e4m3fn [rows][H] (rows = moe_recv_rows), 16-B aligned:
  *             receive regions, source-major.  Slot (s,t,j) with expert e on
- *             rank d = e/L lands at row base[d] + recv_off[d][s]
- *             + (send_pos[s][t][j] - send_off[s][d*L]).
+ *             rank d = e/L and block index u = send_pos[s][t][j] -
+ *             send_off[s][d*L] lands at row base[d] + recv_off[d][s] + u
+ *             (with early rows C: base[d] + s*C + u if u < C, else
+ *             base[d] + N*C + recv_off[d][s] + u - C).
  *   recv_s    fp32 [rows][H/128]: the scale of each 128-element block,
  *             scale = amax/448 (IEEE division), q = e4m3fn_rne_satfinite
  *             (x/scale); an all-zero block has scale 0 and zero bytes.
@@ -264,8 +274,10 @@ int moe_status(void *ws, void *stream, uint32_t *flags);
 /*
  * Copy the routing tables held in ws after moe_dispatch_send into caller
  * arrays (device, int32; any may be NULL): cnt [N][E], send_off [N][E+1],
- * recv_off [N(dest)][N(source)+1], recv_total [N], base [N+1] (first row of
- * each region; base[N] = rows in use when packed, N*R when fixed).
+ * recv_off [N(dest)][N(source)+1] (with early rows: offsets of each
+ * source's rows beyond its first C, from region row N*C), recv_total [N]
+ * (all rows for each destination), base [N+1] (first row of each region;
+ * base[N] = rows in use when packed, N*R when fixed).
  */
 int moe_layout_export(const moe_shape *shape, const void *ws, int32_t *cnt, int32_t *send_off, int32_t *recv_off,
                       int32_t *recv_total, int32_t *base, void *stream);

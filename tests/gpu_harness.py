@@ -25,10 +25,10 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
 
 def run_all(cfg: W.Config, T: int, region_rows: int = 0, idx=None, w=None, x=None, y=None,
             payload: bool = True, combine: bool = True, fill: int | None = 0x5A, device="cuda",
-            single_launch: bool = False):
+            single_launch: bool = False, early_rows: int = 0):
     """Generate (or take) inputs and run dispatch send/recv and combine send/recv
     (single_launch: the send half through moe_dispatch_send_ll)."""
-    sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, region_rows)
+    sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, region_rows, early_rows)
     if idx is None:
         idx, w = W.routing(cfg, T)
     idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(device)

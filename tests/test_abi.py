@@ -56,8 +56,11 @@ def test_region_rows_rejections():
     assert moe.lib.moe_recv_rows(ctypes.byref(moe.shape(16, 128, 2048, 128, 8, region_rows=-1))) == -1
     assert moe.lib.moe_recv_rows(ctypes.byref(moe.shape(16, 128, 2048, 128, 8, region_rows=1 << 28))) == -4
     bad = moe.shape(16, 128, 2048, 128, 8)
-    bad.reserved = 1
+    bad.early_rows = 1                     # early rows need fixed regions
     assert moe.lib.moe_recv_rows(ctypes.byref(bad)) == -1
+    assert moe.lib.moe_recv_rows(ctypes.byref(moe.shape(16, 128, 2048, 128, 8, 100, -1))) == -1
+    assert moe.lib.moe_recv_rows(ctypes.byref(moe.shape(16, 128, 2048, 128, 8, 100, 7))) == -1   # N*C > R
+    assert moe.lib.moe_recv_rows(ctypes.byref(moe.shape(16, 128, 2048, 128, 8, 112, 7))) == 16 * 112
 
 
 def _p(v):

@@ -48,16 +48,16 @@ def _same(a, b, f):
     assert torch.equal(va, vb), f"single launch != multi launch: {f}"
 
 
-def _case(cfg, T, region_rows=0, idx=None, w=None, full=True):
+def _case(cfg, T, region_rows=0, idx=None, w=None, full=True, early_rows=0):
     if idx is None:
         idx, w = W.routing(cfg, T)
-    r = run_all(cfg, T, region_rows, idx=idx, w=w, single_launch=True)
-    lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows)
+    r = run_all(cfg, T, region_rows, idx=idx, w=w, single_launch=True, early_rows=early_rows)
+    lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows, early_rows)
     assert r["flags"] == lay.flags, (r["flags"], lay.flags)
     assert not r["flags"] & moe.FLAG_TIMEOUT
     if full:
         check_full(r, lay)
-    m = run_all(cfg, T, region_rows, idx=r["idx"], w=r["w"], x=r["x"], y=r["y"])
+    m = run_all(cfg, T, region_rows, idx=r["idx"], w=r["w"], x=r["x"], y=r["y"], early_rows=early_rows)
     assert m["flags"] == r["flags"]
     for f in OUTS:
         _same(r, m, f)
@@ -125,6 +125,30 @@ def test_fixed_region_overflow_matches_multi_launch():
     r, lay = _case(cfg, 64, R, idx, w, full=False)
     assert r["flags"] & O.FLAG_OVERFLOW
     assert (r["B"].send_pos.cpu().numpy() == lay.send_pos).all()
+
+
+def _early_region(idx, E, N, C, slack):
+    over = O.layout(idx, E, N, N * C + 10 ** 6, C).recv_off[:, N]
+    return int(N * C + over.max() + slack)
+
+
+@pytest.mark.parametrize("name,C", [("tiny", 1), ("tiny", 48), ("tiny", 200), ("dsv3_decode", 40),
+                                    ("kimi_skewed", 16)])
+def test_early_rows(name, C):
+    """Early rows: the packers of most rows need only their own rank's count."""
+    cfg = W.CONFIGS[name]
+    idx, w = W.routing(cfg, 128)
+    _case(cfg, 128, _early_region(idx, cfg.E, cfg.N, C, 5), idx, w, early_rows=C)
+
+
+def test_early_rows_overflow():
+    cfg = _cfg("ll_early_ovf", N=4, T=64, H=256, E=8, k=2)
+    idx, w = W.routing(cfg, 64)
+    idx = idx.copy()
+    idx[:, :, 0] = 0
+    C = 8
+    r, _ = _case(cfg, 64, _early_region(idx, cfg.E, cfg.N, C, -6), idx, w, full=False, early_rows=C)
+    assert r["flags"] & O.FLAG_OVERFLOW
 
 
 def test_bad_ids():

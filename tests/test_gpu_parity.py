@@ -32,9 +32,9 @@ def _small(name, **kw):
     return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
 
 
-def _full_case(cfg, T, region_rows=0, idx=None, w=None):
-    r = run_all(cfg, T, region_rows, idx=idx, w=w)
-    lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows)
+def _full_case(cfg, T, region_rows=0, idx=None, w=None, early_rows=0):
+    r = run_all(cfg, T, region_rows, idx=idx, w=w, early_rows=early_rows)
+    lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows, early_rows)
     assert r["flags"] == lay.flags, (r["flags"], lay.flags)
     check_full(r, lay)
     return r, lay
@@ -51,6 +51,49 @@ def test_tiny_config_fixed_regions():
     idx, w = W.routing(cfg, 128)
     R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) + 37
     _full_case(cfg, 128, R, idx, w)
+
+
+def _early_region(idx, E, N, C, slack):
+    """Fixed region rows for early rows C: every sender's early rows plus the
+    largest region's further rows, plus `slack` (negative: too small)."""
+    over = O.layout(idx, E, N, N * C + 10 ** 6, C).recv_off[:, N]
+    return int(N * C + over.max() + slack)
+
+
+@pytest.mark.parametrize("C", [1, 48, 200])
+def test_tiny_config_early_rows(C):
+    """Early (private per-sender) rows: C = 1 sends nearly everything through
+    the common part, 200 holds every pair's rows privately."""
+    cfg = W.CONFIGS["tiny"]
+    idx, w = W.routing(cfg, 128)
+    _full_case(cfg, 128, _early_region(idx, cfg.E, cfg.N, C, 17), idx, w, early_rows=C)
+
+
+def test_early_rows_overflow_is_flagged_and_contained():
+    cfg = _small("early_ovf", N=4, T=64, H=256, E=8, k=2)
+    idx, w = W.routing(cfg, 64)
+    idx = idx.copy()
+    idx[:, :, 0] = 0                                   # everybody's slot 0 -> rank 0
+    C = 8
+    R = _early_region(idx, cfg.E, cfg.N, C, -6)
+    r = run_all(cfg, 64, R, idx=idx, w=w, combine=False, early_rows=C)
+    lay = O.layout(idx, cfg.E, cfg.N, R, C)
+    assert r["flags"] & O.FLAG_OVERFLOW and r["flags"] == lay.flags
+    B = r["B"]
+    assert (B.send_pos.cpu().numpy() == lay.send_pos).all()
+    got_rq = B.recv_q.cpu().numpy()
+    x = r["x"].float().cpu().numpy()
+    q, _ = O.quantize_rows(x.reshape(-1, cfg.H))
+    tok = (np.arange(cfg.N)[:, None, None] * 64 + np.arange(64)[None, :, None]) + 0 * idx
+    ok = lay.recv_row >= 0
+    assert not ok.all()
+    assert (got_rq[lay.recv_row[ok]] == q[tok[ok]]).all()
+    rs = B.row_src.cpu().numpy()
+    want = O.row_src(lay)
+    used = O.region_rows_used(lay)
+    for d in range(cfg.N):
+        a = lay.base[d]
+        assert (rs[a:a + used[d]] == want[a:a + used[d]]).all()
 
 
 def test_literal_bound_regions():
