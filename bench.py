@@ -15,7 +15,9 @@ sums (moe_combine_send_partial + moe_combine_recv_partial) are timed after the
 steps, on the same data, and reported beside them; they are not part of the
 step.  So is, when every
 rank's slots fit one routing chunk (T*k <= 4096), the step with the
-single-launch moe_dispatch_send_ll in place of moe_dispatch_send.
+single-launch moe_dispatch_send_ll in place of moe_dispatch_send (also with
+early rows), and the fastest composition of one layer (that dispatch where it
+applies, the unpack, the pulling combine) as whole steps.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -338,6 +340,52 @@ def main():
     copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    # The fastest composition of one layer on one GPU: the dispatch send
+    # (single launch with early rows where it applies, else the multi-launch
+    # call), the unpack, and the pulling combine, timed as whole steps.
+    fast = None
+    if Tc == T:
+        if single is not None:
+            she_f = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, single["early_rows"]["region_rows"],
+                              single["early_rows"]["early_rows"])
+            Bf = moe.allocate(she_f, dev, combine=False)
+            send_f = moe.moe_dispatch_send_ll
+        else:
+            she_f, Bf, send_f = sh, B, moe.moe_dispatch_send
+        yf = y if Bf is B else W.expert_outputs(cfg, Bf.rows, dev)
+        out_f = torch.empty_like(Bc.out)
+        w_f = torch.from_numpy(w).to(dev)
+
+        def step_f(ev=None):
+            if ev: ev[0].record(stream)
+            send_f(she_f, x, idx_d, Bf.recv_q, Bf.recv_s, Bf.send_pos, Bf.ws)
+            if ev: ev[1].record(stream)
+            moe.moe_dispatch_recv(she_f, Bf.recv_q, Bf.recv_s, Bf.ws, Bf.x_q, Bf.x_s, Bf.exp_off, Bf.row_src)
+            if ev: ev[2].record(stream)
+            moe.moe_combine_pull(she_f, yf, idx_d, Bf.send_pos, w_f, Bf.ws, out_f)
+            if ev: ev[3].record(stream)
+
+        for _ in range(args.warmup):
+            step_f()
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_f(evf[i])
+        torch.cuda.synchronize()
+        wall_f = time.perf_counter() - t0
+        ms_f = np.array([[evf[i][p].elapsed_time(evf[i][p + 1]) for p in range(3)] for i in range(args.steps)])
+        fast = {"dispatch_send": send_f.__name__, "early_rows": she_f.early_rows,
+                "us": {n: round(v * 1e3, 1) for n, v in zip(("dispatch_send", "dispatch_recv", "combine_pull"),
+                                                             ms_f.mean(axis=0))},
+                "step_us": round(wall_f * 1e6 / args.steps, 1)}
+        if Bf is not B:
+            flags_f = moe.moe_status(Bf.ws)
+            if flags_f:
+                raise SystemExit(f"device error flags {flags_f:#x} in the fastest-path steps")
+            del Bf, yf
+        del out_f
+
     flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
         raise SystemExit(f"device error flags {flags:#x} in the timed steps")
@@ -390,6 +438,7 @@ def main():
                             "elements_differing_from_send_recv": round(part_diff, 5)},
         "graph_step_us": round(graph_step_ms * 1e3, 1),
         "single_launch_dispatch": single,
+        "fastest_layer": fast,
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -138,6 +138,26 @@ def test_fixed_region_overflow():
     _full_check(r, R)
 
 
+def test_fixed_regions_with_early_rows():
+    """The row lookup follows the early-row layout (its overflow check uses
+    the source-major row)."""
+    cfg = _cfg("cp_early", N=8, T=64, H=256, E=32, k=6)
+    idx, w = W.routing(cfg, 64)
+    C = 20
+    over = O.layout(idx, cfg.E, cfg.N, cfg.N * C + 10 ** 6, C).recv_off[:, cfg.N]
+    R = int(cfg.N * C + over.max() - 3)                  # the fullest region drops its last rows
+    r = run_all(cfg, 64, R, idx=idx, w=w, early_rows=C)
+    assert r["flags"] & O.FLAG_OVERFLOW
+    lay = O.layout(idx, cfg.E, cfg.N, R, C)
+    assert ((lay.em_row < 0) & lay.slot_valid).any()
+    comb, out = _partial(r)
+    comb_o, lead, out_o = O.combine_partial(bf16_np(r["y"]), r["idx"], lay, r["w"])
+    assert (bf16_np(out) == out_o).all()
+    N, T, k = cfg.N, 64, cfg.k
+    rows = [s * T * k + lay.send_pos[s, t, j] for s in range(N) for t in range(T) for j in np.flatnonzero(lead[s, t])]
+    assert (bf16_np(comb).reshape(N * T * k, -1)[rows] == comb_o[rows]).all()
+
+
 def _sampled(r, n_tok=40, seed=3):
     sh, B = r["sh"], r["B"]
     N, T, H, k = sh.N, sh.T, sh.H, sh.k
