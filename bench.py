@@ -390,15 +390,20 @@ def main():
     if flags:
         raise SystemExit(f"device error flags {flags:#x} in the timed steps")
 
-    def info(name, t_ms, t90=None):
+    def info(name, t_ms, t90=None, t50=None):
+        """Mean time t_ms (the roofline uses the mean launch duration), with
+        the p90 and median where given."""
         gbs = nbytes[name] / (t_ms * 1e-3) / 1e9
         d = {"us": round(t_ms * 1e3, 1), "alg_bytes": nbytes[name], "GB/s": round(gbs, 1),
              "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if t50 is not None:
+            d["median_us"] = round(t50 * 1e3, 1)
         if t90 is not None:
             d["p90_us"] = round(t90 * 1e3, 1)
         return d
 
-    phase_info = {name: info(name, per_phase_ms[p], p90_ms[p]) for p, name in enumerate(PHASES)}
+    med_ms = np.median(ms, axis=0)
+    phase_info = {name: info(name, per_phase_ms[p], p90_ms[p], med_ms[p]) for p, name in enumerate(PHASES)}
     if single is not None:
         single["dispatch_send"] = info("dispatch_send", single_ms, single_p90)
         single["early_rows"]["dispatch_send"] = info("dispatch_send", early_ms)
