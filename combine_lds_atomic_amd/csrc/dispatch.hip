@@ -32,7 +32,6 @@
 namespace moe {
 
 constexpr int kPkWaves = kPackShape.waves, kPkThreads = kPackShape.threads();
-constexpr int kUpWaves = kUnpackShape.waves, kUpThreads = kUnpackShape.threads();
 constexpr int kPackCols = kWave * 16;         // elements one wave covers per pass (16 per lane)
 constexpr int kPackPasses = MOE_PACK_PASSES;  // passes whose loads are issued together
 
@@ -552,24 +551,34 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
 }
 
 constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
+// Unpack launch forms (waves per workgroup x workgroups per CU, 16-B loads per
+// lane issued together while copying a row).  Measured in one process: the
+// large form is 2-4% faster from combine-heavy size up, 4% slower at the
+// decode shapes, where the small one stays.
+constexpr LaunchShape kUnpackSmall = MOE_UNPACK_SHAPE;
+constexpr int kUnpackSmallUnroll = 8;
+constexpr LaunchShape kUnpackLarge = {8, 2};
+constexpr int kUnpackLargeUnroll = 32;
+constexpr int64_t kUnpackLargeRows = 131072;   // rows from which the large form is used
 
-__global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
+template <int WAVES, int UNROLL>
+__global__ __launch_bounds__(WAVES * kWave) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
                                                        const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
                                                        float* __restrict__ x_s, int* __restrict__ exp_off,
                                                        int* __restrict__ row_src) {
   __shared__ int svp[kMaxN + 1];
-  for (int i = threadIdx.x; i <= D.N; i += kUpThreads) svp[i] = W.vprefix[i];
+  for (int i = threadIdx.x; i <= D.N; i += (WAVES * kWave)) svp[i] = W.vprefix[i];
   if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kUpThreads) exp_off[i] = W.exp_off[i];
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += (WAVES * kWave)) exp_off[i] = W.exp_off[i];
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int N = D.N, E = D.E, L = D.L;
   const bool scales16 = (D.NB & 3) == 0;   // scale rows are whole 16-byte units
   int lo, hi;
   block_range(svp[N], lo, hi);        // valid rows, in region order
-  for (int g0 = lo + wv; g0 < hi; g0 += kUpWaves * kRowsPerPass) {
+  for (int g0 = lo + wv; g0 < hi; g0 += WAVES * kRowsPerPass) {
     int src = -1, dst = -1;
-    const int g = g0 + lane * kUpWaves;
+    const int g = g0 + lane * WAVES;
     if (lane < kRowsPerPass && g < hi) {
       const int d = floor_index(svp, N + 1, g);
       const int i = g - svp[d];                                  // expert-major row inside region d
@@ -595,7 +604,7 @@ __global__ __launch_bounds__(kUpThreads) void k_unpack(Dims D, Ws W, const uint8
       const int sr = __builtin_amdgcn_readlane(src, r);
       const int dr = __builtin_amdgcn_readlane(dst, r);
       if (sr < 0 || dr < 0) continue;
-      wave_copy16<8>(reinterpret_cast<v4u*>(x_q + (int64_t)dr * D.H),
+      wave_copy16<UNROLL>(reinterpret_cast<v4u*>(x_q + (int64_t)dr * D.H),
                      reinterpret_cast<const v4u*>(recv_q + (int64_t)sr * D.H), D.H / 16, lane);
       if (scales16) {
         const int n16 = D.NB / 4;
@@ -636,9 +645,16 @@ int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, 
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
-  const int grid = stream_grid(kUnpackShape, cus, (int64_t)D.rows, kUpWaves);
-  return launch("k_unpack", k_unpack, dim3(grid), dim3(kUpThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
-                row_src);
+  if ((int64_t)D.rows >= kUnpackLargeRows) {
+    constexpr LaunchShape S = kUnpackLarge;
+    const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
+    return launch("k_unpack", k_unpack<S.waves, kUnpackLargeUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
+                  recv_q, recv_s, x_q, x_s, exp_off, row_src);
+  }
+  constexpr LaunchShape S = kUnpackSmall;
+  const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
+  return launch("k_unpack", k_unpack<S.waves, kUnpackSmallUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
+                recv_q, recv_s, x_q, x_s, exp_off, row_src);
 }
 
 // Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic

@@ -218,13 +218,12 @@ struct LaunchShape {
 #define MOE_UNPACK_SHAPE {16, 1}
 #endif
 #ifndef MOE_COMB_SEND_SHAPE
-#define MOE_COMB_SEND_SHAPE {16, 1}
+#define MOE_COMB_SEND_SHAPE {8, 2}
 #endif
 #ifndef MOE_COMB_RECV_SHAPE
 #define MOE_COMB_RECV_SHAPE {4, 8}
 #endif
 constexpr LaunchShape kPackShape = MOE_PACK_SHAPE;
-constexpr LaunchShape kUnpackShape = MOE_UNPACK_SHAPE;
 constexpr LaunchShape kCombSendShape = MOE_COMB_SEND_SHAPE;
 #ifndef MOE_SEND_PARTIAL_SHAPE
 #define MOE_SEND_PARTIAL_SHAPE {16, 1}
