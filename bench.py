@@ -13,11 +13,11 @@ dispatch at the combine batch.
 The pulling combine (moe_combine_pull) and the combine with send-side partial
 sums (moe_combine_send_partial + moe_combine_recv_partial) are timed after the
 steps, on the same data, and reported beside them; they are not part of the
-step.  So is, when every
-rank's slots fit one routing chunk (T*k <= 4096), the step with the
-single-launch moe_dispatch_send_ll in place of moe_dispatch_send (also with
-early rows), and the fastest composition of one layer (that dispatch where it
-applies, the unpack, the pulling combine) as whole steps.
+step.  So are the direct dispatch (moe_dispatch_direct, in place of send +
+recv), when every rank's slots fit one routing chunk (T*k <= 4096) the step
+with the single-launch moe_dispatch_send_ll in place of moe_dispatch_send
+(also with early rows), and the fastest composition of one layer (the faster
+of these dispatches, the pulling combine) as whole steps.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -53,6 +53,7 @@ def algorithmic_bytes(N, T, H, E, k, Tc=None, G=None):
         "combine_send_partial": Pc * rowb + G * rowb + 3 * N * Tc * k * 4,
         "combine_recv_partial": G * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
         "dispatch_send": N * T * 2 * H + P * rowq + 2 * N * T * k * 4 + N * E * 4,
+        "dispatch_direct": N * T * 2 * H + P * rowq + 3 * N * T * k * 4 + N * E * 4,
         "dispatch_recv": 2 * P * rowq,
         "combine_send": 2 * Pc * rowb,
         "combine_recv": Pc * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
@@ -292,6 +293,23 @@ def main():
                                 "same_send_pos": same_e}
         del Be, ye, comb_e, out_e
 
+    # The direct dispatch (moe_dispatch_direct: rows stored straight at their
+    # expert-major rows, no receive regions, no unpack) on the same inputs
+    # and buffers, compared bit for bit with the two-call path's outputs.
+    ref = {f: getattr(B, f).clone() for f in ("send_pos", "x_q", "x_s", "exp_off", "row_src")}
+    for _ in range(max(args.warmup, 1)):
+        moe.moe_dispatch_direct(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
+    dir_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        dir_ev[i][0].record(stream)
+        moe.moe_dispatch_direct(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
+        dir_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dir_all = np.array([e[0].elapsed_time(e[1]) for e in dir_ev])
+    direct_ms, direct_p90, direct_med = dir_all.mean(), np.percentile(dir_all, 90), np.median(dir_all)
+    direct_same = all(torch.equal(getattr(B, f).view(torch.uint8), ref[f].view(torch.uint8)) for f in ref)
+    del ref
+
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(2):
@@ -340,12 +358,16 @@ def main():
     copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    # The fastest composition of one layer on one GPU: the dispatch send
-    # (single launch with early rows where it applies, else the multi-launch
-    # call), the unpack, and the pulling combine, timed as whole steps.
+    # The fastest composition of one layer on one GPU: the faster dispatch --
+    # the direct one, or the send (single launch with early rows where it
+    # applies, else the multi-launch call) plus the unpack -- then the
+    # pulling combine, timed as whole steps.
     fast = None
     if Tc == T:
-        if single is not None:
+        two_call_ms = (early_ms if single is not None else per_phase_ms[0]) + per_phase_ms[1]
+        if direct_ms < two_call_ms:
+            she_f, Bf, send_f = sh, B, None
+        elif single is not None:
             she_f = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, single["early_rows"]["region_rows"],
                               single["early_rows"]["early_rows"])
             Bf = moe.allocate(she_f, dev, combine=False)
@@ -358,9 +380,13 @@ def main():
 
         def step_f(ev=None):
             if ev: ev[0].record(stream)
-            send_f(she_f, x, idx_d, Bf.recv_q, Bf.recv_s, Bf.send_pos, Bf.ws)
-            if ev: ev[1].record(stream)
-            moe.moe_dispatch_recv(she_f, Bf.recv_q, Bf.recv_s, Bf.ws, Bf.x_q, Bf.x_s, Bf.exp_off, Bf.row_src)
+            if send_f is None:
+                moe.moe_dispatch_direct(she_f, x, idx_d, Bf.x_q, Bf.x_s, Bf.send_pos, Bf.exp_off, Bf.row_src, Bf.ws)
+                if ev: ev[1].record(stream)
+            else:
+                send_f(she_f, x, idx_d, Bf.recv_q, Bf.recv_s, Bf.send_pos, Bf.ws)
+                if ev: ev[1].record(stream)
+                moe.moe_dispatch_recv(she_f, Bf.recv_q, Bf.recv_s, Bf.ws, Bf.x_q, Bf.x_s, Bf.exp_off, Bf.row_src)
             if ev: ev[2].record(stream)
             moe.moe_combine_pull(she_f, yf, idx_d, Bf.send_pos, w_f, Bf.ws, out_f)
             if ev: ev[3].record(stream)
@@ -375,9 +401,11 @@ def main():
         torch.cuda.synchronize()
         wall_f = time.perf_counter() - t0
         ms_f = np.array([[evf[i][p].elapsed_time(evf[i][p + 1]) for p in range(3)] for i in range(args.steps)])
-        fast = {"dispatch_send": send_f.__name__, "early_rows": she_f.early_rows,
-                "us": {n: round(v * 1e3, 1) for n, v in zip(("dispatch_send", "dispatch_recv", "combine_pull"),
-                                                             ms_f.mean(axis=0))},
+        fast = {"dispatch": "moe_dispatch_direct" if send_f is None else f"{send_f.__name__} + moe_dispatch_recv",
+                "early_rows": she_f.early_rows,
+                "us": {n: round(v * 1e3, 1) for n, v in zip(
+                    ("dispatch_direct", None, "combine_pull") if send_f is None else
+                    ("dispatch_send", "dispatch_recv", "combine_pull"), ms_f.mean(axis=0)) if n},
                 "step_us": round(wall_f * 1e6 / args.steps, 1)}
         if Bf is not B:
             flags_f = moe.moe_status(Bf.ws)
@@ -436,6 +464,8 @@ def main():
         "combine_frac": round((nbytes["combine_send"] + nbytes["combine_recv"]) /
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
+        "dispatch_direct": dict(info("dispatch_direct", direct_ms, direct_p90, direct_med),
+                                same_bytes_as_send_recv=bool(direct_same)),
         "combine_partial": {"groups_per_token": round(G / (cfg.N * Tc), 3),
                             "send": info("combine_send_partial", part_ms[0]),
                             "recv": info("combine_recv_partial", part_ms[1]),

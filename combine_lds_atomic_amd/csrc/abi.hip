@@ -177,7 +177,30 @@ int moe_dispatch_send(const moe_shape* shape, const uint16_t* tokens, const int3
   hipStream_t st = as_stream(stream);
   rc = launch_route(D, W, topk_idx, send_pos, st);
   if (rc) return rc;
-  return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s, device_cus(), st);
+  return launch_pack(D, W, tokens, topk_idx, send_pos, recv_q, recv_s, nullptr, nullptr, device_cus(), st);
+}
+
+int moe_dispatch_direct(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* x_q,
+                        float* x_s, int32_t* send_pos, int32_t* exp_off, int32_t* row_src, void* ws, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws || !exp_off) return MOE_ENULL;
+  if (!aligned(ws, kAlign) || !aligned(exp_off, 4)) return MOE_EALIGN;
+  hipStream_t st = as_stream(stream);
+  Ws W;
+  carve(D, ws, &W);
+  if (D.T == 0) {   // empty arrays may be NULL; the layout-only receive half writes exp_off
+    rc = launch_route(D, W, topk_idx, send_pos, st);
+    return rc ? rc : launch_unpack(D, W, nullptr, nullptr, nullptr, nullptr, exp_off, row_src, device_cus(), st);
+  }
+  if (!topk_idx || !send_pos || !row_src) return MOE_ENULL;
+  if (tokens && (!x_q || !x_s)) return MOE_ENULL;
+  if (!aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(row_src, 4)) return MOE_EALIGN;
+  if (tokens && (!aligned(tokens, 16) || !aligned(x_q, 16) || !aligned(x_s, 4))) return MOE_EALIGN;
+  rc = launch_route(D, W, topk_idx, send_pos, st);
+  if (rc) return rc;
+  return launch_pack(D, W, tokens, topk_idx, send_pos, x_q, x_s, row_src, exp_off, device_cus(), st);
 }
 
 int moe_dispatch_send_ll(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* recv_q,

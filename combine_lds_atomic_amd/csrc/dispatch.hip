@@ -155,11 +155,19 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
   pack_scales(D, h0, h1, row, lane, recv_s, ssw);
 }
 
+// DIRECT = false: rows go to the source-major receive regions (recv_q,
+// recv_s).  DIRECT = true: they go straight to their expert-major rows
+// (x_q, x_s), and the kernel also writes row_src and exp_off, the outputs
+// of the receive half, which then has nothing left to do.
+template <bool DIRECT>
 __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                      const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
+                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
+                                                     int* __restrict__ row_src, int* __restrict__ exp_off) {
   __shared__ float sscale[kPkWaves][kMaxNB];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kPkThreads) exp_off[i] = W.exp_off[i];
   int lo, hi;
   block_range(D.N * D.T * D.slices, lo, hi);
   for (int item = lo + wv; item < hi; item += kPkWaves) {
@@ -183,9 +191,23 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
           sp = send_pos[slot];
         }
         const int d = e / D.L;
-        const int r = region_row(D, s, sp - W.send_off[s * (D.E + 1) + d * D.L], W.recv_off[d * (D.N + 1) + s]);
-        const int pr = W.base[d] + r;
-        if ((D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
+        const int* so = W.send_off + s * (D.E + 1);
+        const int r = region_row(D, s, sp - so[d * D.L], W.recv_off[d * (D.N + 1) + s]);   // source-major
+        if (!DIRECT) {
+          const int pr = W.base[d] + r;
+          if ((D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
+        } else {
+          // Expert-major row: the same index k_unpack derives, and the same
+          // rule: it exists if both it and its source-major row fit.
+          const int l = e - d * D.L;
+          const int ie = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + (sp - so[e]);
+          const int pe = W.base[d] + ie;
+          if ((D.R == 0 || ie < D.R) && ie >= 0 && pe < D.rows) {
+            const bool fits = (D.R == 0 || r < D.R) && r >= 0 && W.base[d] + r < D.rows;
+            if (sl == 0) row_src[pe] = fits ? s * D.TK + sp : -1;
+            if (fits) row = pe;
+          }
+        }
       }
     }
     if (x == nullptr) continue;
@@ -634,13 +656,17 @@ static int pack_slices(const Dims& D, int cus, bool payload) {
   return sl;
 }
 
-int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
-                float* recv_s, int cus, hipStream_t st) {
+int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
+                float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st) {
   if (D0.N * D0.T == 0) return MOE_OK;
   Dims D = D0;
   D.slices = pack_slices(D, cus, x != nullptr);
   const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
-  return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, recv_q, recv_s);
+  if (row_src)
+    return launch("k_pack", k_pack<true>, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out,
+                  row_src, exp_off);
+  return launch("k_pack", k_pack<false>, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out,
+                row_src, exp_off);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,

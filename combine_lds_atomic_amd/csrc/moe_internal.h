@@ -292,8 +292,11 @@ __device__ __forceinline__ int floor_index(const int* a, int n, int v, int strid
 
 // Launchers (one per translation unit that owns the kernels).
 int launch_route(const Dims& D, const Ws& W, const int* idx, int* send_pos, hipStream_t st);
-int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* recv_q,
-                float* recv_s, int cus, hipStream_t st);
+// row_src == nullptr: into the source-major receive regions (q_out, s_out =
+// recv_q, recv_s); otherwise straight into the expert-major rows (q_out,
+// s_out = x_q, x_s), also writing row_src and exp_off.
+int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
+                float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st);
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st);
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,

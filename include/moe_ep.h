@@ -163,6 +163,26 @@ int moe_dispatch_send_ll(const moe_shape *shape, const uint16_t *tokens, const i
                          uint8_t *recv_q, float *recv_s, int32_t *send_pos, void *ws, void *stream);
 
 /*
+ * Dispatch in one call, straight into the grouped-GEMM layout ("Dispatch and
+ * combine": peers whose buffers are mapped can push tokens directly; on one
+ * GPU every rank is such a peer).  The same results as moe_dispatch_send
+ * followed by moe_dispatch_recv -- send_pos, x_q, x_s, exp_off, row_src and
+ * the workspace tables, bit for bit -- but each quantised row is stored
+ * once, at its expert-major row, and no source-major receive region is
+ * written or read.
+ *   tokens    bf16 [N][T][H], 16-B aligned, or NULL (layout only: send_pos,
+ *             exp_off, row_src).
+ *   topk_idx  int32 [N][T][k].
+ *   x_q, x_s  out, fp8 [rows][H] and fp32 [rows][H/128], as from
+ *             moe_dispatch_recv (NULL with tokens NULL).
+ *   send_pos, exp_off, row_src   out, as from moe_dispatch_send /
+ *             moe_dispatch_recv.
+ *   ws        workspace of moe_workspace_bytes(shape), initialised once.
+ */
+int moe_dispatch_direct(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx, uint8_t *x_q,
+                        float *x_s, int32_t *send_pos, int32_t *exp_off, int32_t *row_src, void *ws, void *stream);
+
+/*
  * Dispatch, receive half ("Dispatch and combine": the receive buffer is
  * shuffled into the output tensor handed to the grouped GEMM).  Uses only
  * the exchanged counts held in ws.

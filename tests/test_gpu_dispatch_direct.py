@@ -1,0 +1,227 @@
+"""GPU parity of the direct dispatch (moe_dispatch_direct: each row stored
+once, straight at its expert-major row) against the oracle, and against the
+two-call dispatch (moe_dispatch_send + moe_dispatch_recv) bit for bit.
+
+Small shapes compare every element: send_pos, exp_off, the exported tables,
+row_src and the whole x_q / x_s arrays, including the rows nobody writes
+(they keep the fill pattern).  The full-size workloads compare the integer
+outputs and whole arrays with the two-call path, and a sample of rows with
+the oracle."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_lds_atomic_amd as moe
+import workloads as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import check_layout, export_layout, log, run_all  # noqa: E402
+
+FILL = 0x5A
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    log(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _cfg(name, **kw):
+    return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
+
+
+def _direct(r, payload=True, fill=FILL):
+    """The direct dispatch of run_all's inputs into buffers of its own."""
+    sh = r["sh"]
+    B = moe.allocate(sh, "cuda", payload=payload, combine=False, fill_rows=fill)
+    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).cuda()
+    moe.moe_dispatch_direct(sh, r["x"] if payload else None, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off,
+                            B.row_src, B.ws)
+    torch.cuda.synchronize()
+    return B
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+def _same_as_two_calls(r, B2):
+    B1 = r["B"]
+    for f in ("send_pos", "exp_off", "row_src", "x_q", "x_s"):
+        a, b = getattr(B1, f), getattr(B2, f)
+        if a is None:
+            assert b is None
+            continue
+        assert torch.equal(_bits(a), _bits(b)), f
+    g1, g2 = export_layout(r), export_layout(dict(r, B=B2))
+    for key in g1:
+        assert (g1[key] == g2[key]).all(), key
+    flags = moe.moe_status(B2.ws)   # read and cleared
+    assert flags == r["flags"]
+    return flags
+
+
+def _check_oracle(r, B2, lay):
+    """Every element against the oracle (small shapes)."""
+    check_layout(dict(r, B=B2), lay)
+    if B2.x_q is None:
+        return
+    rq, rs = O.dispatch_send(r["x"].float().cpu().numpy(), lay)
+    xq, xs, _ = O.dispatch_recv(rq, rs, lay)
+    got_q, got_s = B2.x_q.cpu().numpy(), B2.x_s.cpu().numpy()
+    erow = lay.em_row[lay.em_row >= 0]
+    assert (got_q[erow] == xq[erow]).all(), "x_q"
+    assert (got_s[erow].view(np.uint32) == xs[erow].view(np.uint32)).all(), "x_s"
+    untouched = np.setdiff1d(np.arange(B2.rows), erow)
+    assert (got_q[untouched] == FILL).all(), "x_q rows without a slot were written"
+    assert (got_s[untouched] == float(FILL)).all(), "x_s rows without a slot were written"
+
+
+def _case(cfg, T, region_rows=0, idx=None, w=None, early_rows=0, payload=True):
+    r = run_all(cfg, T, region_rows, idx=idx, w=w, payload=payload, combine=False, early_rows=early_rows)
+    B2 = _direct(r, payload)
+    flags = _same_as_two_calls(r, B2)
+    lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows, early_rows)
+    _check_oracle(r, B2, lay)
+    return r, B2, lay, flags
+
+
+def test_tiny_config():
+    _case(W.CONFIGS["tiny"], 128)
+
+
+def test_tiny_config_fixed_regions():
+    cfg = W.CONFIGS["tiny"]
+    idx, w = W.routing(cfg, 128)
+    R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) + 17
+    _case(cfg, 128, R, idx=idx, w=w)
+
+
+def test_layout_only():
+    _case(W.CONFIGS["tiny"], 128, payload=False)
+
+
+@pytest.mark.parametrize("N,T,H,E,k", [
+    (8, 33, 256, 16, 8),        # k = E/N
+    (5, 77, 1152, 40, 6),       # 9 scale blocks per row (not whole 16-byte units), ragged
+    (4, 20, 256, 64, 12),       # k > 8
+    (2, 5, 128, 4, 1),          # one slot per token
+    (16, 9, 384, 16, 4),        # one expert per rank
+    (3, 1500, 384, 12, 3),      # many tokens, ragged workgroup ranges
+    (6, 40, 9216, 24, 4),       # long rows: the pack splits tokens into slices
+])
+def test_shapes(N, T, H, E, k):
+    _case(_cfg(f"dd{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k), T)
+
+
+def test_bad_ids():
+    cfg = _cfg("dd_badid", N=4, T=40, H=256, E=16, k=4)
+    idx, w = W.routing(cfg, 40)
+    idx = idx.copy()
+    idx[0, 3, 1] = 16
+    idx[2, 7, 0] = -1
+    idx[3, 39, 3] = 1 << 30
+    flags = _case(cfg, 40, idx=idx, w=w)[3]
+    assert flags & O.FLAG_BADID
+
+
+def test_fixed_region_overflow():
+    """The fullest regions drop rows: the same rows are dropped (and the same
+    row_src holes left) as by the two-call path."""
+    cfg = _cfg("dd_ovf", N=4, T=64, H=256, E=8, k=3)
+    idx, w = W.routing(cfg, 64)
+    idx = idx.copy()
+    idx[:, :, 0] = 0
+    R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) - 9
+    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w)
+    assert flags & O.FLAG_OVERFLOW
+    assert ((lay.em_row < 0) & lay.slot_valid).any()
+
+
+@pytest.mark.parametrize("C,slack", [(20, 40), (20, -3), (56, -2)])
+def test_early_rows(C, slack):
+    """Early rows.  With C = 56 some sources leave early rows unused, so the
+    fullest region drops source-major rows while every expert-major row still
+    fits: those rows exist with row_src -1 and keep their fill."""
+    cfg = _cfg("dd_early", N=8, T=64, H=256, E=32, k=6)
+    idx, w = W.routing(cfg, 64)
+    over = O.layout(idx, cfg.E, cfg.N, cfg.N * C + 10 ** 6, C).recv_off[:, cfg.N]
+    R = int(cfg.N * C + over.max() + slack)
+    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w, early_rows=C)
+    if slack < 0:
+        assert flags & O.FLAG_OVERFLOW
+    if C == 56:
+        assert (B2.row_src.cpu().numpy() == -1).sum() == 3
+
+
+def test_empty_batch():
+    sh = moe.shape(4, 0, 256, 16, 2)
+    B = moe.allocate(sh, "cuda", combine=False)
+    B.exp_off.fill_(-5)
+    empty_i = torch.empty((4, 0, 2), dtype=torch.int32, device="cuda")
+    moe.moe_dispatch_direct(sh, None, empty_i, None, None, None, B.exp_off, None, B.ws)
+    torch.cuda.synchronize()
+    assert (B.exp_off.cpu().numpy() == 0).all()
+    assert moe.moe_status(B.ws) == 0
+
+
+def test_then_combine():
+    """The direct dispatch's row_src drives the combine exactly as the
+    two-call path's does."""
+    cfg = W.CONFIGS["tiny"]
+    r = run_all(cfg, 128)
+    B2 = _direct(r)
+    comb = torch.empty_like(r["B"].comb)
+    out = torch.empty_like(r["B"].out)
+    comb.view(torch.int16).fill_(0x3F00)
+    w_d = torch.from_numpy(np.ascontiguousarray(r["w"], np.float32)).cuda()
+    moe.moe_combine_send(r["sh"], r["y"], B2.row_src, B2.ws, comb)
+    moe.moe_combine_recv(r["sh"], comb, B2.send_pos, w_d, out)
+    torch.cuda.synchronize()
+    assert torch.equal(comb.view(torch.int16), r["B"].comb.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), r["B"].out.view(torch.int16))
+
+
+# ------------------------------------------------------------------ full size
+
+def _need(gib):
+    free, _ = torch.cuda.mem_get_info()
+    if free < gib * 2 ** 30:
+        pytest.skip(f"needs {gib} GiB of free device memory, {free / 2**30:.0f} GiB free")
+
+
+def _full(cfg, T, n_tok=48, seed=5):
+    r = run_all(cfg, T, combine=False)
+    B2 = _direct(r)
+    _same_as_two_calls(r, B2)
+    sh = r["sh"]
+    N, H, k = sh.N, sh.H, sh.k
+    lay = O.layout(r["idx"], sh.E, N)
+    check_layout(dict(r, B=B2), lay)
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([rng.choice(N * T, n_tok, replace=False), [0, N * T - 1]]))
+    s_, t_ = np.divmod(toks, T)
+    xs = r["x"].reshape(N * T, H)[torch.from_numpy(toks).cuda()].float().cpu().numpy()
+    q, sc = O.quantize_rows(xs)
+    rr = lay.em_row[s_, t_, :]
+    ok = rr >= 0
+    ri = torch.from_numpy(rr[ok]).cuda()
+    assert (B2.x_q[ri].cpu().numpy() == np.repeat(q[:, None, :], k, axis=1)[ok]).all()
+    assert (B2.x_s[ri].cpu().numpy().view(np.uint32) == np.repeat(sc[:, None, :], k, axis=1)[ok].view(np.uint32)).all()
+
+
+def test_dsv3_decode_full_size():
+    cfg = W.CONFIGS["dsv3_decode"]
+    _full(cfg, cfg.T)
+
+
+def test_combine_heavy_full_size():
+    _need(30)
+    cfg = W.CONFIGS["combine_heavy"]
+    _full(cfg, cfg.T)
