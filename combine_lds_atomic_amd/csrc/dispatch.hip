@@ -11,6 +11,10 @@
 //             the receive side finds each row's (expert, source) segment from
 //             the exchanged counts alone and copies it out of the
 //             source-major receive region.
+//   k_pack_direct  k_pack storing each row at its expert-major row instead
+//             (peers mapped into each other's memory push straight into the
+//             grouped-GEMM layout; on one GPU every rank is such a peer), so
+//             neither the receive regions nor k_unpack are needed.
 #include <map>
 #include <mutex>
 
@@ -155,15 +159,16 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
   pack_scales(D, h0, h1, row, lane, recv_s, ssw);
 }
 
-// DIRECT = false: rows go to the source-major receive regions (recv_q,
-// recv_s).  DIRECT = true: they go straight to their expert-major rows
-// (x_q, x_s), and the kernel also writes row_src and exp_off, the outputs
-// of the receive half, which then has nothing left to do.
+// The pack loop.  DIRECT = false: rows go to the source-major receive
+// regions (recv_q, recv_s).  DIRECT = true: they go straight to their
+// expert-major rows (x_q, x_s), and the loop also writes row_src and
+// exp_off, the outputs of the receive half, which then has nothing left to
+// do.
 template <bool DIRECT>
-__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
-                                                     const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
-                                                     int* __restrict__ row_src, int* __restrict__ exp_off) {
+__device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
+                                            const int* __restrict__ idx, int* __restrict__ send_pos,
+                                            uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
+                                            int* __restrict__ row_src, int* __restrict__ exp_off) {
   __shared__ float sscale[kPkWaves][kMaxNB];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
@@ -213,6 +218,19 @@ __global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_
     if (x == nullptr) continue;
     pack_item<false>(D, item, row, x, recv_q, recv_s, sscale[wv]);
   }
+}
+
+__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                     const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
+  pack_tokens<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
+}
+
+__global__ __launch_bounds__(kPkThreads) void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                            const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                            uint8_t* __restrict__ x_q, float* __restrict__ x_s,
+                                                            int* __restrict__ row_src, int* __restrict__ exp_off) {
+  pack_tokens<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
 }
 
 // ------------------------------------------------------------------ single launch
@@ -663,10 +681,9 @@ int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, 
   D.slices = pack_slices(D, cus, x != nullptr);
   const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
   if (row_src)
-    return launch("k_pack", k_pack<true>, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out,
-                  row_src, exp_off);
-  return launch("k_pack", k_pack<false>, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out,
-                row_src, exp_off);
+    return launch("k_pack_direct", k_pack_direct, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out,
+                  s_out, row_src, exp_off);
+  return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
