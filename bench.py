@@ -14,10 +14,11 @@ The pulling combine (moe_combine_pull) and the combine with send-side partial
 sums (moe_combine_send_partial + moe_combine_recv_partial) are timed after the
 steps, on the same data, and reported beside them; they are not part of the
 step.  So are the direct dispatch (moe_dispatch_direct, in place of send +
-recv), when every rank's slots fit one routing chunk (T*k <= 4096) the step
-with the single-launch moe_dispatch_send_ll in place of moe_dispatch_send
-(also with early rows), and the fastest composition of one layer (the faster
-of these dispatches, the pulling combine) as whole steps.
+recv), when every rank's slots fit one routing chunk (T*k <= 4096) its single
+launch (moe_dispatch_direct_ll) and the step with the single-launch
+moe_dispatch_send_ll in place of moe_dispatch_send (also with early rows),
+and the fastest composition of one layer (the fastest of these dispatches,
+the pulling combine) as whole steps.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -296,18 +297,24 @@ def main():
     # The direct dispatch (moe_dispatch_direct: rows stored straight at their
     # expert-major rows, no receive regions, no unpack) on the same inputs
     # and buffers, compared bit for bit with the two-call path's outputs.
+    # Its single launch (moe_dispatch_direct_ll) likewise where T*k <= 4096.
     ref = {f: getattr(B, f).clone() for f in ("send_pos", "x_q", "x_s", "exp_off", "row_src")}
-    for _ in range(max(args.warmup, 1)):
-        moe.moe_dispatch_direct(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
-    dir_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        dir_ev[i][0].record(stream)
-        moe.moe_dispatch_direct(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
-        dir_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dir_all = np.array([e[0].elapsed_time(e[1]) for e in dir_ev])
-    direct_ms, direct_p90, direct_med = dir_all.mean(), np.percentile(dir_all, 90), np.median(dir_all)
-    direct_same = all(torch.equal(getattr(B, f).view(torch.uint8), ref[f].view(torch.uint8)) for f in ref)
+
+    def time_direct(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        same = all(torch.equal(getattr(B, f).view(torch.uint8), ref[f].view(torch.uint8)) for f in ref)
+        return t.mean(), np.percentile(t, 90), np.median(t), bool(same)
+
+    direct_ms, direct_p90, direct_med, direct_same = time_direct(moe.moe_dispatch_direct)
+    direct_ll = time_direct(moe.moe_dispatch_direct_ll) if T * cfg.k <= 4096 and T > 0 else None
     del ref
 
     # The pulling combine on the same data (not part of the step).
@@ -365,7 +372,10 @@ def main():
     fast = None
     if Tc == T:
         two_call_ms = (early_ms if single is not None else per_phase_ms[0]) + per_phase_ms[1]
-        if direct_ms < two_call_ms:
+        direct_f = moe.moe_dispatch_direct
+        if direct_ll is not None and direct_ll[0] < direct_ms:
+            direct_f = moe.moe_dispatch_direct_ll
+        if min(direct_ms, direct_ll[0] if direct_ll else direct_ms) < two_call_ms:
             she_f, Bf, send_f = sh, B, None
         elif single is not None:
             she_f = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, single["early_rows"]["region_rows"],
@@ -381,7 +391,7 @@ def main():
         def step_f(ev=None):
             if ev: ev[0].record(stream)
             if send_f is None:
-                moe.moe_dispatch_direct(she_f, x, idx_d, Bf.x_q, Bf.x_s, Bf.send_pos, Bf.exp_off, Bf.row_src, Bf.ws)
+                direct_f(she_f, x, idx_d, Bf.x_q, Bf.x_s, Bf.send_pos, Bf.exp_off, Bf.row_src, Bf.ws)
                 if ev: ev[1].record(stream)
             else:
                 send_f(she_f, x, idx_d, Bf.recv_q, Bf.recv_s, Bf.send_pos, Bf.ws)
@@ -401,7 +411,7 @@ def main():
         torch.cuda.synchronize()
         wall_f = time.perf_counter() - t0
         ms_f = np.array([[evf[i][p].elapsed_time(evf[i][p + 1]) for p in range(3)] for i in range(args.steps)])
-        fast = {"dispatch": "moe_dispatch_direct" if send_f is None else f"{send_f.__name__} + moe_dispatch_recv",
+        fast = {"dispatch": direct_f.__name__ if send_f is None else f"{send_f.__name__} + moe_dispatch_recv",
                 "early_rows": she_f.early_rows,
                 "us": {n: round(v * 1e3, 1) for n, v in zip(
                     ("dispatch_direct", None, "combine_pull") if send_f is None else
@@ -465,7 +475,9 @@ def main():
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
         "dispatch_direct": dict(info("dispatch_direct", direct_ms, direct_p90, direct_med),
-                                same_bytes_as_send_recv=bool(direct_same)),
+                                same_bytes_as_send_recv=bool(direct_same),
+                                single_launch=None if direct_ll is None else dict(
+                                    info("dispatch_direct", *direct_ll[:3]), same_bytes_as_send_recv=direct_ll[3])),
         "combine_partial": {"groups_per_token": round(G / (cfg.N * Tc), 3),
                             "send": info("combine_send_partial", part_ms[0]),
                             "recv": info("combine_recv_partial", part_ms[1]),

@@ -97,6 +97,9 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->tbase = take64((size_t)D.N);
   W->tready = take64((size_t)kReadyCopies * kReadyStride);
   W->tcdone = take64((size_t)D.N * kReadyStride);
+  W->temr = take64((size_t)D.N * D.E);
+  W->tlim = take64((size_t)D.N * D.N);
+  W->tcold = take64((size_t)D.N * kReadyStride);
   return o;
 }
 
@@ -216,8 +219,31 @@ int moe_dispatch_send_ll(const moe_shape* shape, const uint16_t* tokens, const i
   if (tokens && (!recv_q || !recv_s)) return MOE_ENULL;
   if (!aligned(topk_idx, 4) || !aligned(send_pos, 4)) return MOE_EALIGN;
   if (tokens && (!aligned(tokens, 16) || !aligned(recv_q, 16) || !aligned(recv_s, 4))) return MOE_EALIGN;
-  return launch_dispatch_ll(D, W_of(D, ws), tokens, topk_idx, send_pos, recv_q, recv_s, device_cus(),
-                            as_stream(stream));
+  return launch_dispatch_ll(D, W_of(D, ws), tokens, topk_idx, send_pos, recv_q, recv_s, nullptr, nullptr,
+                            device_cus(), as_stream(stream));
+}
+
+int moe_dispatch_direct_ll(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* x_q,
+                           float* x_s, int32_t* send_pos, int32_t* exp_off, int32_t* row_src, void* ws,
+                           void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  if (!ws || !exp_off) return MOE_ENULL;
+  if (!aligned(ws, kAlign) || !aligned(exp_off, 4)) return MOE_EALIGN;
+  hipStream_t st = as_stream(stream);
+  Ws W;
+  carve(D, ws, &W);
+  if (D.T == 0) {   // nothing to exchange; empty arrays may be NULL
+    rc = launch_route(D, W, topk_idx, send_pos, st);
+    return rc ? rc : launch_unpack(D, W, nullptr, nullptr, nullptr, nullptr, exp_off, row_src, device_cus(), st);
+  }
+  if (D.B != 1) return MOE_EINVAL;   // more than one routing chunk per rank
+  if (!topk_idx || !send_pos || !row_src) return MOE_ENULL;
+  if (tokens && (!x_q || !x_s)) return MOE_ENULL;
+  if (!aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(row_src, 4)) return MOE_EALIGN;
+  if (tokens && (!aligned(tokens, 16) || !aligned(x_q, 16) || !aligned(x_s, 4))) return MOE_EALIGN;
+  return launch_dispatch_ll(D, W, tokens, topk_idx, send_pos, x_q, x_s, row_src, exp_off, device_cus(), st);
 }
 
 int moe_dispatch_recv(const moe_shape* shape, const uint8_t* recv_q, const float* recv_s, const void* ws,

@@ -16,6 +16,7 @@
 //             grouped-GEMM layout; on one GPU every rank is such a peer), so
 //             neither the receive regions nor k_unpack are needed.
 #include <map>
+#include <tuple>
 #include <mutex>
 
 #include "route_dev.h"
@@ -265,13 +266,13 @@ __global__ __launch_bounds__(kPkThreads) void k_pack_direct(Dims D, Ws W, const 
 // replicated "ready" words, published after the values they need, then read
 // their values (normally already there, otherwise they keep polling those).
 
-// v[u] = value of p[u * stride] for u < n (n <= M), once all carry `tag`;
-// false after kSpinLimit polls.
-template <int M>
-__device__ __forceinline__ bool tag_wait_n(const uint64_t* p, int64_t stride, int n, uint32_t tag, int (&v)[M]) {
+// v[u] = value at addr(u) for u < n (n <= M), once all carry `tag`; false
+// after kSpinLimit polls.
+template <int M, class Addr>
+__device__ __forceinline__ bool tag_gather(Addr addr, int n, uint32_t tag, int (&v)[M]) {
   uint64_t u[M];
 #pragma unroll
-  for (int i = 0; i < M; ++i) u[i] = i < n ? tag_load(p + i * stride) : ((uint64_t)tag << 32);
+  for (int i = 0; i < M; ++i) u[i] = i < n ? tag_load(addr(i)) : ((uint64_t)tag << 32);
   for (int it = 0;; ++it) {
     bool ok = true;
 #pragma unroll
@@ -281,11 +282,17 @@ __device__ __forceinline__ bool tag_wait_n(const uint64_t* p, int64_t stride, in
     __builtin_amdgcn_s_sleep(2);
 #pragma unroll
     for (int i = 0; i < M; ++i)
-      if (!tag_ok(u[i], tag)) u[i] = tag_load(p + i * stride);
+      if (!tag_ok(u[i], tag)) u[i] = tag_load(addr(i));
   }
 #pragma unroll
   for (int i = 0; i < M; ++i) v[i] = (int)(uint32_t)u[i];
   return true;
+}
+
+// v[u] = value of p[u * stride] for u < n (n <= M).
+template <int M>
+__device__ __forceinline__ bool tag_wait_n(const uint64_t* p, int64_t stride, int n, uint32_t tag, int (&v)[M]) {
+  return tag_gather<M>([&](int i) { return p + i * stride; }, n, tag, v);
 }
 
 // Three tagged values at once (p2 may be NULL: v2 is left as it is).
@@ -314,13 +321,25 @@ constexpr int kCrossBatch = 4;
 inline size_t cross_ll_lds_bytes(int E) { return sizeof(int) * ((size_t)2 * kThreads + E + 1); }
 
 // The cross-rank role: the same tables k_route_cross computes, from the
-// tagged send offsets and counts of the count workgroups.
-__device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int* wsum) {
+// tagged send offsets and counts of the count workgroups.  In the direct
+// form (exp_out != nullptr) the packers need only the column workgroups'
+// values: this role first waits for those and signals the packers, then
+// computes the tables (for moe_layout_export, moe_dispatch_recv's
+// successors and the combine) and copies exp_off to exp_out.
+__device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int* wsum, int* exp_out) {
   const int N = D.N, E = D.E, L = D.L, tid = threadIdx.x;
   int* part = sm;                  // [G][N], G*N <= kThreads: rows beyond the early ones
   int* partc = sm + kThreads;      // [G][N]: all rows
   int* ex = sm + 2 * kThreads;     // [E+1]
   bool ok = true;
+  if (exp_out) {
+    for (int dd = tid; dd < N && ok; dd += kThreads) {
+      int one;
+      ok = tag_wait(W.tcold + dd * kReadyStride, tag, &one);
+    }
+    __syncthreads();
+    if (tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
+  }
 
   // (1) rows from source s to destination d are
   // send_off[s][(d+1)L] - send_off[s][dL]; thread (g, d) sums them over its
@@ -407,7 +426,7 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
     }
   }
   __syncthreads();
-  if (tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
+  if (!exp_out && tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
 
   // (4) Off the packers' path: src_in_exp and exp_off for dispatch_recv.
   for (int e = tid; e < E; e += kThreads) {
@@ -443,8 +462,125 @@ __device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int*
   for (int i = tid; i < N * (L + 1); i += kThreads) {
     const int dd = i / (L + 1), l = i - dd * (L + 1);
     W.exp_off[i] = ex[dd * L + l] - ex[dd * L];
+    if (exp_out) exp_out[i] = ex[dd * L + l] - ex[dd * L];
   }
   if (!ok) atomicOr(W.err, MOE_FLAG_TIMEOUT);
+}
+
+// LDS ints of the column role: counts, then their column scans, [N][L]
+// each; the senders' offsets to ranks d and d+1, [N] each; the expert
+// totals and their scan [L+1]; the rows beyond the early ones per source,
+// then their scan [N].
+inline size_t column_ll_lds_bytes(int N, int E) { return sizeof(int) * ((size_t)2 * E + 3 * N + E / N + 1); }
+
+// The column role of the direct form, for destination rank d.  From the
+// tagged counts and send offsets alone it publishes what a packer needs for
+// every row bound for d, so the packers do not wait for the cross-rank role:
+//   temr[s][e]  what a packer of source s adds to a sender position of
+//               expert e = d*L + l to get the row's expert-major row,
+//               base[d] + exp_off[d][l] + src_in_exp[s][e] - send_off[s][e]
+//               (packed regions: base[d] = sum over s of send_off[s][d*L],
+//               the slots all sources send to ranks before d);
+//   tlim[s][d]  (fixed regions) the sender positions below which the row's
+//               source-major row fits region d: send_off[s][d*L] + C +
+//               max(0, R - N*C - recv_off[d][s]) with C early rows (0: none);
+// then tcold[d].
+__device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* sm, int* wsum) {
+  const int N = D.N, L = D.L, E = D.E, NL = N * L, tid = threadIdx.x;
+  int* c = sm;               // [N][L] counts of rank d's experts, then send_off[s][e]
+  int* sie = sm + NL;        // [N][L] src_in_exp[s][e]
+  int* so0 = sm + 2 * NL;    // [N] send_off[s][d*L]
+  int* so1 = so0 + N;        // [N] send_off[s][(d+1)*L]
+  int* ov = so1 + N;         // [N] rows beyond the early ones from s, then recv_off[d][s]
+  int* eo = ov + N;          // [L+1] totals, then exp_off[d][l]
+  // (1) The counts and the senders' offsets, kCrossBatch values per thread
+  // at a time: indices below NL are counts, then send_off[s][d*L], then
+  // send_off[s][(d+1)*L].
+  bool ok = true;
+  const int nv = NL + 2 * N;
+  for (int i0 = tid * kCrossBatch; i0 < nv && ok; i0 += kThreads * kCrossBatch) {
+    const int n = min(kCrossBatch, nv - i0);
+    int v[kCrossBatch] = {};
+    ok = tag_gather<kCrossBatch>(
+        [&](int u) {
+          const int i = i0 + u;
+          if (i < NL) return W.tcnt + (int64_t)(i / L) * E + d * L + i % L;
+          const int j = i - NL, hi = j >= N;
+          return W.toff + (int64_t)(j - hi * N) * (N + 1) + d + hi;
+        },
+        n, tag, v);
+    for (int u = 0; u < n; ++u) {
+      const int i = i0 + u;
+      if (i < NL) c[i] = v[u];
+      else so0[i - NL] = v[u];   // so0 and so1 are adjacent
+    }
+  }
+  const bool fail = __syncthreads_or(!ok);
+  // (2) Per source: rows beyond the early ones; per expert: column scans
+  // over sources.
+  for (int s = tid; s < N && !fail; s += kThreads) ov[s] = max(so1[s] - so0[s] - D.Ce, 0);
+  for (int l = tid; l < L && !fail; l += kThreads) {
+    int acc = 0;
+    for (int s = 0; s < N; ++s) {
+      sie[s * L + l] = acc;
+      acc += c[s * L + l];
+    }
+    eo[l] = acc;
+  }
+  __syncthreads();
+  // (3) Per source: send_off[s][e] over rank d's experts, and recv_off[d][s]
+  // (exclusive scan of the rows beyond the early ones; one thread, N <= 256).
+  for (int s = tid; s < N && !fail; s += kThreads) {
+    int acc = so0[s];
+    for (int l = 0; l < L; ++l) {
+      const int t = c[s * L + l];
+      c[s * L + l] = acc;
+      acc += t;
+    }
+  }
+  if (tid == 0 && !fail) {
+    int acc = 0;
+    for (int s = 0; s < N; ++s) {
+      const int t = ov[s];
+      ov[s] = acc;
+      acc += t;
+    }
+  }
+  // (4) exp_off[d][l]: exclusive scan of the totals, four per thread (L <= 1024),
+  // and the packed region base: the sum of send_off[s][d*L] over sources.
+  int bd;
+  {
+    const int l0 = min(L, tid * 4), l1 = min(L, l0 + 4);
+    int v = 0;
+    for (int l = l0; l < l1; ++l) v += eo[l];
+    int all;
+    int x = block_scan<kThreads>(v, wsum, &all);
+    for (int l = l0; l < l1; ++l) {
+      const int t = eo[l];
+      eo[l] = x;
+      x += t;
+    }
+    int b = 0;
+    for (int s = tid; s < N; s += kThreads) b += so0[s];
+    block_scan<kThreads>(b, wsum, &bd);
+    if (D.R) bd = d * D.R;
+  }
+  __syncthreads();
+  if (!fail) {
+    for (int i = tid; i < NL; i += kThreads) {
+      const int s = i / L, l = i - s * L;
+      tag_put(W.temr + (int64_t)s * E + d * L + l, tag, bd + eo[l] + sie[i] - c[i]);
+    }
+    if (D.R)
+      for (int s = tid; s < N; s += kThreads)
+        tag_put(W.tlim + (int64_t)s * N + d, tag, so0[s] + D.Ce + max(0, D.R - N * D.Ce - ov[s]));
+  }
+  __syncthreads();
+  if (fail) {
+    if (tid == 0) atomicOr(W.err, MOE_FLAG_TIMEOUT);
+  } else if (tid == 0) {
+    tag_put(W.tcold + d * kReadyStride, tag, 1);
+  }
 }
 
 static_assert(kPkThreads == kThreads, "the single-launch dispatch runs every role with 256 threads");
@@ -452,10 +588,20 @@ static_assert(kPkThreads == kThreads, "the single-launch dispatch runs every rol
 // LDS bytes of the pack role (per-wave scales of one token row).
 inline size_t pack_lds_bytes(int NB) { return sizeof(float) * (size_t)kPkWaves * NB; }
 
-__global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const uint16_t* __restrict__ x,
-                                                          const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
-                                                          int npack) {
+// The single launch.  DIRECT = false: rows go to the receive regions
+// (recv_q, recv_s).  DIRECT = true: N column workgroups (after the count
+// workgroups, before the cross-rank one) publish, per destination rank,
+// each (source, expert)'s offset into the expert-major layout and the
+// source-major fit limits; the cross-rank workgroup signals the packers once
+// all columns are out, then computes the workspace tables and copies
+// exp_off out; the packers store every row at its expert-major row (recv_q,
+// recv_s = x_q, x_s) and write row_src.  Without tokens (x == nullptr) the
+// direct form still runs its packers, for row_src.
+template <bool DIRECT>
+__device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
+                                            const int* __restrict__ idx, int* __restrict__ send_pos,
+                                            uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
+                                            int* __restrict__ row_src, int* __restrict__ exp_out, int npack) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int wsum[kWavesPerBlock + 1];
   __shared__ int sh_fail;
@@ -470,14 +616,17 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
   __syncthreads();
   const uint32_t tag = epoch_tag(sh_epoch);
 
+  const int ncol = DIRECT ? D.N : 0;   // column workgroups
   if (wg < D.N) {
     count_chunk(D, W, idx, send_pos, wg, 0, smem, wsum, tag);
     __syncthreads();
     if (threadIdx.x == 0) tag_put(W.tcdone + wg * kReadyStride, tag, 1);
-  } else if (wg == D.N) {
-    cross_ll(D, W, tag, reinterpret_cast<int*>(smem), wsum);
+  } else if (DIRECT && wg < D.N + ncol) {
+    column_ll(D, W, tag, wg - D.N, reinterpret_cast<int*>(smem), wsum);
+  } else if (wg == D.N + ncol) {
+    cross_ll(D, W, tag, reinterpret_cast<int*>(smem), wsum, DIRECT ? exp_out : nullptr);
   } else {
-    const int p = wg - D.N - 1;
+    const int p = wg - D.N - ncol - 1;
     const int items = D.N * D.T * D.slices;
     const int lo = (int)((int64_t)items * p / npack), hi = (int)((int64_t)items * (p + 1) / npack);
     bool fail = false;
@@ -488,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
       if (threadIdx.x == 0 && lo < hi) {
         int one;
         bool ok;
-        if (D.Ce == 0) {
+        if (DIRECT || D.Ce == 0) {
           ok = tag_wait(W.tready + (p % kReadyCopies) * kReadyStride, tag, &one);
         } else {
           const int s_first = lo / D.slices / D.T, s_last = (hi - 1) / D.slices / D.T;
@@ -519,7 +668,22 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
       bool ok = true;
       if (!fail && lane < D.k) {
         const int64_t slot = (int64_t)tok * D.k + lane;
-        if (e >= 0 && e < D.E) {
+        if (DIRECT && e >= 0 && e < D.E) {
+          // The column workgroup's values: the expert-major row offset and,
+          // with fixed regions, the limit below which the source-major row
+          // fits (the rule of k_unpack: the row exists if it fits region d,
+          // its payload only if the source-major row fits too).
+          const int d = e / D.L;
+          int sp = 0, off = 0, lim = 0;
+          ok = tag_wait3(W.tpos + slot, W.temr + (int64_t)s * D.E + e, D.R ? W.tlim + (int64_t)s * D.N + d : nullptr,
+                         tag, sp, off, lim);
+          const int pe = off + sp, ie = pe - (D.R ? d * D.R : 0);
+          if (ok && (D.R == 0 || ie < D.R) && ie >= 0 && pe < D.rows) {
+            const bool fits = D.R == 0 || sp < lim;
+            if (item % D.slices == 0) row_src[pe] = fits ? s * D.TK + sp : -1;
+            if (fits) row = pe;
+          }
+        } else if (e >= 0 && e < D.E) {
           const int d = e / D.L;
           int sp = 0, rel = 0, bd = D.R ? d * D.R : 0, r = -1;
           if (D.Ce == 0) {
@@ -552,6 +716,11 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
     const int wv = threadIdx.x / kWave;
     float* ssw = reinterpret_cast<float*>(smem) + wv * D.NB;
     int item = lo + wv;
+    if (DIRECT && x == nullptr) {   // layout only: positions and row_src
+      gate();
+      for (; item < hi; item += kPkWaves) resolve(item, expert(item));
+      item = hi;
+    }
     const bool has = item < hi;
     v4u a[kPackPasses], b[kPackPasses];
     int e1 = -1;
@@ -561,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
       load_chunk(x + (int64_t)tok * D.H, h0, h1, threadIdx.x & (kWave - 1), a, b);
       e1 = expert(item);
     }
-    gate();
+    if (!DIRECT || x != nullptr) gate();
     if (has) {
       pack_item<true>(D, item, resolve(item, e1), x, recv_q, recv_s, ssw, a, b);
       item += kPkWaves;
@@ -588,6 +757,21 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const ui
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                          const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
+                                                          int npack) {
+  dispatch_ll<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr, npack);
+}
+
+__global__ __launch_bounds__(kThreads) void k_dispatch_ll_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                                 const int* __restrict__ idx,
+                                                                 int* __restrict__ send_pos, uint8_t* __restrict__ x_q,
+                                                                 float* __restrict__ x_s, int* __restrict__ row_src,
+                                                                 int* __restrict__ exp_off, int npack) {
+  dispatch_ll<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off, npack);
 }
 
 constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
@@ -708,42 +892,48 @@ int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float
 #ifndef MOE_LL_BLOCKS_PER_CU
 #define MOE_LL_BLOCKS_PER_CU 6
 #endif
-static int ll_blocks_per_cu(size_t lds) {
+static int ll_blocks_per_cu(const void* kernel, size_t lds) {
   static std::mutex mu;
-  static std::map<std::pair<int, size_t>, int> cache;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   std::lock_guard<std::mutex> g(mu);
-  auto it = cache.find({dev, lds});
+  auto it = cache.find({dev, kernel, lds});
   if (it != cache.end()) return it->second;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(k_dispatch_ll), kThreads, lds) !=
-          hipSuccess ||
-      nb < 1)
-    nb = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, lds) != hipSuccess || nb < 1) nb = 1;
   if (nb > MOE_LL_BLOCKS_PER_CU) nb = MOE_LL_BLOCKS_PER_CU;
-  cache[{dev, lds}] = nb;
+  cache[{dev, kernel, lds}] = nb;
   return nb;
 }
 
 int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos,
-                       uint8_t* recv_q, float* recv_s, int cus, hipStream_t st) {
+                       uint8_t* q_out, float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st) {
   if (D0.B != 1 || D0.N * D0.T == 0) return MOE_EINVAL;
+  const bool direct = row_src != nullptr;
   Dims D = D0;
   D.slices = pack_slices(D, cus, x != nullptr);
   size_t lds = count_lds_bytes(D.E);
   lds = lds > cross_ll_lds_bytes(D.E) ? lds : cross_ll_lds_bytes(D.E);
   lds = lds > pack_lds_bytes(D.NB) ? lds : pack_lds_bytes(D.NB);
+  if (direct) lds = lds > column_ll_lds_bytes(D.N, D.E) ? lds : column_ll_lds_bytes(D.N, D.E);
+  const void* kernel = direct ? reinterpret_cast<const void*>(k_dispatch_ll_direct)
+                              : reinterpret_cast<const void*>(k_dispatch_ll);
+  const int layout_wgs = D.N + 1 + (direct ? D.N : 0);
   // Packers: as many as the k_pack grid would have, but no more than fit on
-  // the GPU beside the N + 1 layout workgroups, so no packer starts late.
+  // the GPU beside the layout workgroups, so no packer starts late.  The
+  // direct form needs packers without tokens too (they write row_src).
   int npack = 0;
-  if (x) {
-    const int resident = cus * ll_blocks_per_cu(lds) - (D.N + 1);
+  if (x || direct) {
+    const int resident = cus * ll_blocks_per_cu(kernel, lds) - layout_wgs;
     npack = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
     if (resident >= 1 && npack > resident) npack = resident;
   }
-  return launch("k_dispatch_ll", k_dispatch_ll, dim3(D.N + 1 + npack), dim3(kThreads), lds, st, D, W, x, idx,
-                send_pos, recv_q, recv_s, npack);
+  if (direct)
+    return launch("k_dispatch_ll_direct", k_dispatch_ll_direct, dim3(layout_wgs + npack), dim3(kThreads), lds, st, D,
+                  W, x, idx, send_pos, q_out, s_out, row_src, exp_off, npack);
+  return launch("k_dispatch_ll", k_dispatch_ll, dim3(layout_wgs + npack), dim3(kThreads), lds, st, D, W, x, idx,
+                send_pos, q_out, s_out, npack);
 }
 
 }  // namespace moe

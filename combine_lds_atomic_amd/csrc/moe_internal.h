@@ -91,6 +91,10 @@ struct Ws {
   uint64_t *tbase;    // [N] region bases
   uint64_t *tready;   // [kReadyCopies][kReadyStride]: published after the values packers need
   uint64_t *tcdone;   // [N][kReadyStride]: rank s's count work is published (early rows)
+  // Direct form only (rows stored at their expert-major rows):
+  uint64_t *temr;     // [N][E] base[d] + exp_off[d][l] + src_in_exp[s][e] - send_off[s][e], e = d*L + l
+  uint64_t *tlim;     // [N][N] fixed regions: sender positions of s below this fit region d
+  uint64_t *tcold;    // [N][kReadyStride]: the column of destination d is published
 };
 
 // Copies of the "ready" word, one per 64-byte line, so that the waiting
@@ -305,8 +309,11 @@ int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, c
                      hipStream_t st);
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st);
+// row_src == nullptr: into the receive regions (q_out, s_out = recv_q,
+// recv_s); otherwise the direct form, into the expert-major rows (x_q, x_s),
+// also writing row_src and exp_off.
 int launch_dispatch_ll(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos,
-                       uint8_t* recv_q, float* recv_s, int cus, hipStream_t st);
+                       uint8_t* q_out, float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st);
 int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                              const float* w, uint16_t* comb, int cus, hipStream_t st);
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,

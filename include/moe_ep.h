@@ -68,8 +68,9 @@ extern "C" {
 #define MOE_FLAG_BADID 1u    /* a top-k id outside [0, E): that slot was dropped  */
 #define MOE_FLAG_OVERFLOW 2u /* a fixed region got more rows than region_rows     */
 #define MOE_FLAG_BOUND 4u    /* a region count exceeded N*T*max(k, E/N)           */
-#define MOE_FLAG_TIMEOUT 8u  /* moe_dispatch_send_ll: a wait inside the launch gave
-                                up (its rows were dropped); re-initialise ws     */
+#define MOE_FLAG_TIMEOUT 8u  /* moe_dispatch_send_ll / moe_dispatch_direct_ll: a wait
+                                inside the launch gave up (its rows were dropped);
+                                re-initialise ws                                  */
 
 /*
  * Problem shape, per logical rank, identical on all N ranks.
@@ -110,7 +111,7 @@ int64_t moe_recv_rows(const moe_shape *shape);
 int64_t moe_workspace_bytes(const moe_shape *shape);
 
 /* Zero the workspace header (the error word) and, when every rank fits one
- * routing chunk (T*k <= 4096), the exchange area of moe_dispatch_send_ll.
+ * routing chunk (T*k <= 4096), the exchange area of the single-launch calls.
  * Call once after allocating a workspace, before its first use, and again
  * before using it for another shape.  ws: device, 256-B aligned. */
 int moe_workspace_init(const moe_shape *shape, void *ws, void *stream);
@@ -181,6 +182,21 @@ int moe_dispatch_send_ll(const moe_shape *shape, const uint16_t *tokens, const i
  */
 int moe_dispatch_direct(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx, uint8_t *x_q,
                         float *x_s, int32_t *send_pos, int32_t *exp_off, int32_t *row_src, void *ws, void *stream);
+
+/*
+ * moe_dispatch_direct in a single launch, for decode-sized batches (the
+ * low-latency mode of the AWS China blog "750B MoE model migration from a
+ * self-built RoCE cluster to AWS EFA", section 4.4: one kernel, no host in
+ * the loop).  Same arguments, results and workspace tables as
+ * moe_dispatch_direct, with the limits and the exchange protocol of
+ * moe_dispatch_send_ll: every rank's slots must fit one routing chunk
+ * (T*k <= 4096, else MOE_EINVAL), and a wait inside the launch that gives up
+ * sets MOE_FLAG_TIMEOUT and drops its rows.  tokens may be NULL (layout
+ * only).
+ */
+int moe_dispatch_direct_ll(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx, uint8_t *x_q,
+                           float *x_s, int32_t *send_pos, int32_t *exp_off, int32_t *row_src, void *ws,
+                           void *stream);
 
 /*
  * Dispatch, receive half ("Dispatch and combine": the receive buffer is

@@ -11,7 +11,7 @@ import combine_lds_atomic_amd as moe
 
 def test_exports_every_declared_symbol():
     declared = moe.declared_symbols()
-    assert {"moe_dispatch_send", "moe_dispatch_send_ll", "moe_dispatch_direct", "moe_dispatch_recv", "moe_combine_send",
+    assert {"moe_dispatch_send", "moe_dispatch_send_ll", "moe_dispatch_direct", "moe_dispatch_direct_ll", "moe_dispatch_recv", "moe_combine_send",
             "moe_combine_recv", "moe_combine_pull"} <= set(declared)
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -88,6 +88,10 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     assert lib.moe_dispatch_direct(s, _p(A + 8), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -3
     assert lib.moe_dispatch_direct(s, _p(A), _p(A), _p(A + 8), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -3
     assert lib.moe_dispatch_direct(s, _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A + 16), None) == -3
+    assert lib.moe_dispatch_direct_ll(s, _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), None, None) == -2
+    assert lib.moe_dispatch_direct_ll(s, _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), None, _p(A), None) == -2
+    assert lib.moe_dispatch_direct_ll(s, _p(A + 8), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -3
+    assert lib.moe_dispatch_direct_ll(big, _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), _p(A), None) == -1
     assert lib.moe_dispatch_recv(s, _p(A), _p(A), _p(A), None, _p(A), _p(A), _p(A), None) == -2  # partial payload
     assert lib.moe_dispatch_recv(s, _p(A), _p(A), _p(A), _p(A + 4), _p(A), _p(A), _p(A), None) == -3
     assert lib.moe_combine_send(s, _p(A), _p(A), _p(A), None, None) == -2

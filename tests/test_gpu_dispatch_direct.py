@@ -1,6 +1,7 @@
-"""GPU parity of the direct dispatch (moe_dispatch_direct: each row stored
-once, straight at its expert-major row) against the oracle, and against the
-two-call dispatch (moe_dispatch_send + moe_dispatch_recv) bit for bit.
+"""GPU parity of the direct dispatch (moe_dispatch_direct, and its single
+launch moe_dispatch_direct_ll: each row stored once, straight at its
+expert-major row) against the oracle, and against the two-call dispatch
+(moe_dispatch_send + moe_dispatch_recv) bit for bit.
 
 Small shapes compare every element: send_pos, exp_off, the exported tables,
 row_src and the whole x_q / x_s arrays, including the rows nobody writes
@@ -36,13 +37,25 @@ def _cfg(name, **kw):
     return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
 
 
-def _direct(r, payload=True, fill=FILL):
-    """The direct dispatch of run_all's inputs into buffers of its own."""
+CALLS = {"direct": moe.moe_dispatch_direct, "direct_ll": moe.moe_dispatch_direct_ll}
+
+
+@pytest.fixture(params=list(CALLS))
+def call(request):
+    return request.param
+
+
+def _fits_ll(T, k):
+    return T * k <= 4096
+
+
+def _direct(r, payload=True, fill=FILL, call="direct", B=None):
+    """The direct dispatch of run_all's inputs into buffers of its own (or B)."""
     sh = r["sh"]
-    B = moe.allocate(sh, "cuda", payload=payload, combine=False, fill_rows=fill)
+    if B is None:
+        B = moe.allocate(sh, "cuda", payload=payload, combine=False, fill_rows=fill)
     idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).cuda()
-    moe.moe_dispatch_direct(sh, r["x"] if payload else None, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off,
-                            B.row_src, B.ws)
+    CALLS[call](sh, r["x"] if payload else None, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
     torch.cuda.synchronize()
     return B
 
@@ -83,28 +96,30 @@ def _check_oracle(r, B2, lay):
     assert (got_s[untouched] == float(FILL)).all(), "x_s rows without a slot were written"
 
 
-def _case(cfg, T, region_rows=0, idx=None, w=None, early_rows=0, payload=True):
+def _case(cfg, T, region_rows=0, idx=None, w=None, early_rows=0, payload=True, call="direct"):
+    if call == "direct_ll" and not _fits_ll(T, cfg.k):
+        pytest.skip("the single launch needs T*k <= 4096")
     r = run_all(cfg, T, region_rows, idx=idx, w=w, payload=payload, combine=False, early_rows=early_rows)
-    B2 = _direct(r, payload)
+    B2 = _direct(r, payload, call=call)
     flags = _same_as_two_calls(r, B2)
     lay = O.layout(r["idx"], cfg.E, cfg.N, region_rows, early_rows)
     _check_oracle(r, B2, lay)
     return r, B2, lay, flags
 
 
-def test_tiny_config():
-    _case(W.CONFIGS["tiny"], 128)
+def test_tiny_config(call):
+    _case(W.CONFIGS["tiny"], 128, call=call)
 
 
-def test_tiny_config_fixed_regions():
+def test_tiny_config_fixed_regions(call):
     cfg = W.CONFIGS["tiny"]
     idx, w = W.routing(cfg, 128)
     R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) + 17
-    _case(cfg, 128, R, idx=idx, w=w)
+    _case(cfg, 128, R, idx=idx, w=w, call=call)
 
 
-def test_layout_only():
-    _case(W.CONFIGS["tiny"], 128, payload=False)
+def test_layout_only(call):
+    _case(W.CONFIGS["tiny"], 128, payload=False, call=call)
 
 
 @pytest.mark.parametrize("N,T,H,E,k", [
@@ -116,22 +131,22 @@ def test_layout_only():
     (3, 1500, 384, 12, 3),      # many tokens, ragged workgroup ranges
     (6, 40, 9216, 24, 4),       # long rows: the pack splits tokens into slices
 ])
-def test_shapes(N, T, H, E, k):
-    _case(_cfg(f"dd{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k), T)
+def test_shapes(N, T, H, E, k, call):
+    _case(_cfg(f"dd{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k), T, call=call)
 
 
-def test_bad_ids():
+def test_bad_ids(call):
     cfg = _cfg("dd_badid", N=4, T=40, H=256, E=16, k=4)
     idx, w = W.routing(cfg, 40)
     idx = idx.copy()
     idx[0, 3, 1] = 16
     idx[2, 7, 0] = -1
     idx[3, 39, 3] = 1 << 30
-    flags = _case(cfg, 40, idx=idx, w=w)[3]
+    flags = _case(cfg, 40, idx=idx, w=w, call=call)[3]
     assert flags & O.FLAG_BADID
 
 
-def test_fixed_region_overflow():
+def test_fixed_region_overflow(call):
     """The fullest regions drop rows: the same rows are dropped (and the same
     row_src holes left) as by the two-call path."""
     cfg = _cfg("dd_ovf", N=4, T=64, H=256, E=8, k=3)
@@ -139,13 +154,13 @@ def test_fixed_region_overflow():
     idx = idx.copy()
     idx[:, :, 0] = 0
     R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) - 9
-    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w)
+    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w, call=call)
     assert flags & O.FLAG_OVERFLOW
     assert ((lay.em_row < 0) & lay.slot_valid).any()
 
 
 @pytest.mark.parametrize("C,slack", [(20, 40), (20, -3), (56, -2)])
-def test_early_rows(C, slack):
+def test_early_rows(C, slack, call):
     """Early rows.  With C = 56 some sources leave early rows unused, so the
     fullest region drops source-major rows while every expert-major row still
     fits: those rows exist with row_src -1 and keep their fill."""
@@ -153,30 +168,30 @@ def test_early_rows(C, slack):
     idx, w = W.routing(cfg, 64)
     over = O.layout(idx, cfg.E, cfg.N, cfg.N * C + 10 ** 6, C).recv_off[:, cfg.N]
     R = int(cfg.N * C + over.max() + slack)
-    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w, early_rows=C)
+    r, B2, lay, flags = _case(cfg, 64, R, idx=idx, w=w, early_rows=C, call=call)
     if slack < 0:
         assert flags & O.FLAG_OVERFLOW
     if C == 56:
         assert (B2.row_src.cpu().numpy() == -1).sum() == 3
 
 
-def test_empty_batch():
+def test_empty_batch(call):
     sh = moe.shape(4, 0, 256, 16, 2)
     B = moe.allocate(sh, "cuda", combine=False)
     B.exp_off.fill_(-5)
     empty_i = torch.empty((4, 0, 2), dtype=torch.int32, device="cuda")
-    moe.moe_dispatch_direct(sh, None, empty_i, None, None, None, B.exp_off, None, B.ws)
+    CALLS[call](sh, None, empty_i, None, None, None, B.exp_off, None, B.ws)
     torch.cuda.synchronize()
     assert (B.exp_off.cpu().numpy() == 0).all()
     assert moe.moe_status(B.ws) == 0
 
 
-def test_then_combine():
+def test_then_combine(call):
     """The direct dispatch's row_src drives the combine exactly as the
     two-call path's does."""
     cfg = W.CONFIGS["tiny"]
     r = run_all(cfg, 128)
-    B2 = _direct(r)
+    B2 = _direct(r, call=call)
     comb = torch.empty_like(r["B"].comb)
     out = torch.empty_like(r["B"].out)
     comb.view(torch.int16).fill_(0x3F00)
@@ -188,6 +203,31 @@ def test_then_combine():
     assert torch.equal(out.view(torch.int16), r["B"].out.view(torch.int16))
 
 
+def test_single_launch_workspace_reuse():
+    """One workspace through direct_ll, send_ll and direct_ll again with a
+    new routing (each call advances the workspace's call number): every
+    result equals a fresh workspace's."""
+    cfg = _cfg("dd_reuse", N=8, T=96, H=512, E=64, k=6)
+    sh = moe.shape(cfg.N, 96, cfg.H, cfg.E, cfg.k)
+    Bs = moe.allocate(sh, "cuda", combine=False, fill_rows=FILL)
+    for rnd, call in enumerate(["direct_ll", "send_ll", "direct_ll", "direct_ll"]):
+        idx, w = W.routing(cfg.with_(seed=cfg.seed + rnd), 96)
+        r = run_all(cfg, 96, idx=idx, w=w, combine=False)
+        if call == "send_ll":
+            idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+            moe.moe_dispatch_send_ll(sh, r["x"], idx_d, Bs.recv_q, Bs.recv_s, Bs.send_pos, Bs.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(Bs.send_pos, r["B"].send_pos)
+            assert torch.equal(Bs.recv_q, r["B"].recv_q)
+            assert moe.moe_status(Bs.ws) == 0
+            continue
+        Bs.x_q.fill_(FILL)
+        Bs.x_s.fill_(float(FILL))
+        Bs.row_src.fill_(FILL)
+        _direct(r, call=call, B=Bs)
+        _same_as_two_calls(r, Bs)
+
+
 # ------------------------------------------------------------------ full size
 
 def _need(gib):
@@ -196,9 +236,11 @@ def _need(gib):
         pytest.skip(f"needs {gib} GiB of free device memory, {free / 2**30:.0f} GiB free")
 
 
-def _full(cfg, T, n_tok=48, seed=5):
+def _full(cfg, T, n_tok=48, seed=5, call="direct"):
+    if call == "direct_ll" and not _fits_ll(T, cfg.k):
+        pytest.skip("the single launch needs T*k <= 4096")
     r = run_all(cfg, T, combine=False)
-    B2 = _direct(r)
+    B2 = _direct(r, call=call)
     _same_as_two_calls(r, B2)
     sh = r["sh"]
     N, H, k = sh.N, sh.H, sh.k
@@ -216,9 +258,14 @@ def _full(cfg, T, n_tok=48, seed=5):
     assert (B2.x_s[ri].cpu().numpy().view(np.uint32) == np.repeat(sc[:, None, :], k, axis=1)[ok].view(np.uint32)).all()
 
 
-def test_dsv3_decode_full_size():
+def test_dsv3_decode_full_size(call):
     cfg = W.CONFIGS["dsv3_decode"]
-    _full(cfg, cfg.T)
+    _full(cfg, cfg.T, call=call)
+
+
+def test_kimi_dispatch_full_size(call):
+    cfg = W.CONFIGS["kimi_skewed"]
+    _full(cfg, cfg.T, call=call)
 
 
 def test_combine_heavy_full_size():
