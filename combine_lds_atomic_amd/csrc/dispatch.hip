@@ -214,6 +214,8 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
             if (fits) row = pe;
           }
         }
+      } else if (D.B > 1 && sl == 0) {
+        send_pos[slot] = -1;   // a dropped slot (the count kernel marks it when it writes positions itself)
       }
     }
     if (x == nullptr) continue;

@@ -171,6 +171,22 @@ def test_bad_ids_are_dropped_and_flagged():
     check_full(r, lay)
 
 
+def test_bad_ids_with_several_routing_chunks():
+    """T*k > 4096: positions come from chunk bases, and a dropped slot's
+    send_pos is still -1."""
+    cfg = _small("badid_chunks", N=2, T=700, H=256, E=16, k=8)
+    idx, w = W.routing(cfg, 700)
+    idx = idx.copy()
+    idx[0, 3, 1] = 16
+    idx[1, 650, 7] = -1
+    idx[1, 699, 0] = 1 << 30
+    r = run_all(cfg, 700, idx=idx, w=w)
+    lay = O.layout(idx, cfg.E, cfg.N)
+    assert r["flags"] & O.FLAG_BADID and lay.flags & O.FLAG_BADID
+    assert (lay.send_pos[idx < 0] == -1).all()
+    check_full(r, lay)
+
+
 def test_fixed_region_overflow_is_flagged_and_contained():
     cfg = _small("ovf", N=4, T=64, H=256, E=8, k=2)
     idx, w = W.routing(cfg, 64)
