@@ -105,6 +105,41 @@ __device__ __forceinline__ int em_row_of(const Dims& D, const Ws& W, int s, int 
   return (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) ? p : -1;
 }
 
+// With fixed regions that overflowed, a valid slot can be left without an
+// expert-major row (its own index or its source-major row did not fit).  No
+// row_src entry names its comb row, so k_comb_send never writes it; this
+// kernel writes it as zeros instead, so that the receive half's sum skips
+// the slot exactly (adding w * +0 leaves a float32 sum unchanged, and the
+// sum, starting at +0, never holds -0), as the pulling combine does.  Comb
+// rows at positions no valid slot has are left untouched.  Without an
+// overflow every workgroup returns after reading the region totals.
+__global__ __launch_bounds__(kThreads) void k_comb_zero_dropped(Dims D, Ws W, uint16_t* __restrict__ comb) {
+  __shared__ int over;
+  if (threadIdx.x == 0) over = 0;
+  __syncthreads();
+  for (int d = threadIdx.x; d < D.N; d += kThreads)
+    if (W.recv_total[d] > D.R || D.N * D.Ce + W.recv_off[d * (D.N + 1) + D.N] > D.R) atomicOr(&over, 1);
+  __syncthreads();
+  if (!over) return;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int n16 = D.H / 8;
+  int lo, hi;
+  block_range(D.N * D.TK, lo, hi);   // comb rows s*T*k + sender position
+  for (int p0 = lo + wv * kWave; p0 < hi; p0 += kWavesPerBlock * kWave) {
+    const int pos = p0 + lane;
+    bool drop = false;
+    if (pos < hi) {
+      const int s = pos / D.TK, p = pos - s * D.TK;
+      const int* so = W.send_off + s * (D.E + 1);
+      if (p < so[D.E]) drop = em_row_of(D, W, s, floor_index(so, D.E + 1, p), p) < 0;
+    }
+    for (uint64_t m = __ballot(drop); m; m &= m - 1) {
+      v4u* row = reinterpret_cast<v4u*>(comb + (int64_t)(p0 + __builtin_ctzll(m)) * D.H);
+      for (int c = lane; c < n16; c += kWave) st16(row + c, v4u{0, 0, 0, 0});
+    }
+  }
+}
+
 // Per lane j < k: whether slot j leads its group, i.e. has a row (dest >= 0)
 // and no earlier slot of the token has a row on the same rank.
 __device__ __forceinline__ bool group_leader(int dest, int k, int lane) {
@@ -372,7 +407,11 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
   const int grid = stream_grid(kCombSendShape, cus, (int64_t)D.rows, kCsWaves);
-  return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
+  const int rc = launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
+  if (rc || D.R == 0) return rc;   // packed regions never overflow
+  const int64_t need = ((int64_t)D.N * D.TK + kThreads - 1) / kThreads;
+  const int zgrid = (int)(need < (int64_t)cus * 4 ? need : (int64_t)cus * 4);
+  return launch("k_comb_zero_dropped", k_comb_zero_dropped, dim3(zgrid), dim3(kThreads), 0, st, D, W, comb);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,

@@ -224,8 +224,12 @@ int moe_dispatch_recv(const moe_shape *shape, const uint8_t *recv_q, const float
  *          as x_q (the grouped GEMM's output).
  *   row_src  as written by moe_dispatch_recv.
  *   comb   bf16 [N][T*k][H] out, 16-B aligned: comb[row_src[i]] = y_em[i].
- *          It may alias memory no longer needed by dispatch ("buffers are
- *          reused between dispatch and combine").
+ *          With fixed regions, the row of a valid slot that an overflow left
+ *          without an expert-major row (so no row_src names it) is written
+ *          as zeros, so that moe_combine_recv skips it exactly; rows at
+ *          positions no valid slot has are untouched.  It may alias memory
+ *          no longer needed by dispatch ("buffers are reused between
+ *          dispatch and combine").
  */
 int moe_combine_send(const moe_shape *shape, const uint16_t *y_em, const int32_t *row_src, const void *ws,
                      uint16_t *comb, void *stream);

@@ -372,7 +372,9 @@ def combine_send(y_em, rsrc, N: int, T: int, k: int):
     """y_em: bfloat16 bits uint16 [rows, H] in expert-major order.
 
     Returns comb uint16 [N*T*k, H]: comb[row_src[i]] = y_em[i]; rows no slot
-    returns to stay zero here (the library leaves them untouched)."""
+    returns to stay zero here (the library writes zeros only for the rows of
+    valid slots that a full fixed region dropped, and leaves positions no
+    valid slot has untouched)."""
     rows, H = y_em.shape
     comb = np.zeros((N * T * k, H), np.uint16)
     ok = rsrc >= 0

@@ -115,6 +115,11 @@ def check_full(r, lay: O.Layout, check_comb=True):
         got_comb = bf16_np(B.comb).reshape(N * T * k, H)
         wr = rsrc[rsrc >= 0]
         assert (got_comb[wr] == comb[wr]).all(), "comb"
+        # a valid slot left without a row by a full fixed region: a zero row
+        lost = lay.slot_valid & (lay.em_row < 0)
+        if lost.any():
+            s_, t_, j_ = np.nonzero(lost)
+            assert (got_comb[s_ * T * k + lay.send_pos[s_, t_, j_]] == 0).all(), "comb rows of dropped slots"
         out = O.combine_recv(comb, lay.send_pos, r["w"], T, k)
         got_out = bf16_np(B.out)
         check_combine_out(got_out, out)
@@ -132,3 +137,103 @@ def check_combine_out(got: np.ndarray, ref: np.ndarray):
     assert (d <= np.maximum(ulp, 2.0 ** -133)).all(), f"combine off by more than 1 ulp: max {d.max()}"
     assert (d <= 2.0 ** -7 * np.abs(f) + 1e-3).all(), "combine outside abs/rel tolerance"
     assert (got == ref).all(), f"combine not bit-exact at {np.count_nonzero(got != ref)} elements"
+
+
+# ------------------------------------------------------------------ direct dispatch
+
+DIRECT_CALLS = {"direct": moe.moe_dispatch_direct, "direct_ll": moe.moe_dispatch_direct_ll}
+
+
+def run_direct(r, call="direct", payload=True, fill=0x5A, B=None):
+    """The direct dispatch of run_all's inputs into buffers of its own (or B)."""
+    sh = r["sh"]
+    if B is None:
+        B = moe.allocate(sh, r["B"].ws.device, payload=payload, combine=False, fill_rows=fill)
+    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).to(B.ws.device)
+    DIRECT_CALLS[call](sh, r["x"] if payload else None, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src,
+                       B.ws)
+    torch.cuda.synchronize()
+    return B
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+def check_same_as_two_calls(r, B2):
+    """Every output and workspace table of a direct dispatch (B2) equals the
+    two-call path's (r["B"]) bit for bit; returns B2's status word."""
+    B1 = r["B"]
+    for f in ("send_pos", "exp_off", "row_src", "x_q", "x_s"):
+        a, b = getattr(B1, f), getattr(B2, f)
+        if a is None:
+            assert b is None
+            continue
+        assert torch.equal(_bits(a), _bits(b)), f
+    g1, g2 = export_layout(r), export_layout(dict(r, B=B2))
+    for key in g1:
+        assert (g1[key] == g2[key]).all(), key
+    flags = moe.moe_status(B2.ws)   # read and cleared
+    assert flags == r["flags"]
+    return flags
+
+
+# ------------------------------------------------------------------ send-side partial combine
+
+PARTIAL_FILL = 0x3F00
+
+
+def run_partial(r):
+    """Both halves of the partial combine on the buffers of a run_all result."""
+    sh, B = r["sh"], r["B"]
+    dev = B.ws.device
+    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).to(dev)
+    w_d = torch.from_numpy(np.ascontiguousarray(r["w"], np.float32)).to(dev)
+    comb = torch.empty_like(B.comb)
+    comb.view(torch.int16).fill_(PARTIAL_FILL)
+    out = torch.full_like(B.out, 3.0)
+    moe.moe_combine_send_partial(sh, r["y"], idx_d, B.send_pos, w_d, B.ws, comb)
+    moe.moe_combine_recv_partial(sh, comb, idx_d, B.send_pos, B.ws, out)
+    assert moe.moe_status(B.ws) & moe.FLAG_TIMEOUT == 0
+    return comb, out
+
+
+def partial_bound_check(out_bits, rows_by_slot, w_tok, group_rows):
+    """The partial combine's tolerance against the float64 sum, one token."""
+    o = O.bf16_from_bits(out_bits).astype(np.float64)
+    ww = np.asarray(w_tok, np.float64)[:, None]
+    exact = (ww * rows_by_slot).sum(axis=0)
+    mag = (np.abs(ww) * np.abs(rows_by_slot)).sum(axis=0)
+    pg = sum(np.abs(O.bf16_from_bits(p).astype(np.float64)) for p in group_rows) if group_rows else 0.0
+    k = len(w_tok)
+    lim = 2.0 ** -8 * (np.abs(o) + pg) + 2 * k * 2.0 ** -24 * mag + 2.0 ** -133
+    assert (np.abs(o - exact) <= lim).all()
+
+
+def check_partial_full(r, lay):
+    """Whole-buffer parity of the partial combine against combine_partial:
+    group rows at their leaders, untouched rows, the output, and the bound."""
+    sh = r["sh"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    comb, out = run_partial(r)
+    y = bf16_np(r["y"])
+    comb_o, lead, out_o = O.combine_partial(y, r["idx"], lay, r["w"])
+    got_comb = bf16_np(comb).reshape(N * T * k, H)
+    led = np.zeros(N * T * k, bool)
+    for s in range(N):
+        for t in range(T):
+            for j in np.flatnonzero(lead[s, t]):
+                led[s * T * k + lay.send_pos[s, t, j]] = True
+    assert (got_comb[led] == comb_o[led]).all(), "group rows"
+    assert (got_comb[~led] == PARTIAL_FILL).all(), "rows no group leads were written"
+    got_out = bf16_np(out)
+    assert (got_out == out_o).all(), f"out differs at {np.count_nonzero(got_out != out_o)} elements"
+    yv = O.bf16_from_bits(y).astype(np.float64)
+    for s in range(N):
+        for t in range(T):
+            part = lay.em_row[s, t] >= 0
+            rows = np.zeros((k, H))
+            rows[part] = yv[lay.em_row[s, t][part]]
+            grp = [comb_o[s * T * k + lay.send_pos[s, t, j]] for j in np.flatnonzero(lead[s, t])]
+            partial_bound_check(got_out[s, t], rows, np.where(part, r["w"][s, t], 0.0), grp)
+    return lead

@@ -15,15 +15,15 @@ import numpy as np
 import pytest
 import torch
 
-import combine_lds_atomic_amd as moe
 import workloads as W
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import bf16_np, log, run_all  # noqa: E402
+from gpu_harness import (PARTIAL_FILL, bf16_np, check_partial_full, log, partial_bound_check,  # noqa: E402
+                         run_all, run_partial)
 
-FILL = 0x3F00
+FILL = PARTIAL_FILL
 
 
 @pytest.fixture(autouse=True)
@@ -38,58 +38,14 @@ def _cfg(name, **kw):
     return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
 
 
-def _partial(r):
-    """Run both halves on the buffers of a run_all result."""
-    sh, B = r["sh"], r["B"]
-    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).cuda()
-    w_d = torch.from_numpy(np.ascontiguousarray(r["w"], np.float32)).cuda()
-    comb = torch.empty_like(B.comb)
-    comb.view(torch.int16).fill_(FILL)
-    out = torch.full_like(B.out, 3.0)
-    moe.moe_combine_send_partial(sh, r["y"], idx_d, B.send_pos, w_d, B.ws, comb)
-    moe.moe_combine_recv_partial(sh, comb, idx_d, B.send_pos, B.ws, out)
-    assert moe.moe_status(B.ws) & moe.FLAG_TIMEOUT == 0
-    return comb, out
-
-
-def _bound_check(out_bits, rows_by_slot, w_tok, group_rows):
-    """The derived tolerance against the float64 sum, one token."""
-    o = O.bf16_from_bits(out_bits).astype(np.float64)
-    ww = np.asarray(w_tok, np.float64)[:, None]
-    exact = (ww * rows_by_slot).sum(axis=0)
-    mag = (np.abs(ww) * np.abs(rows_by_slot)).sum(axis=0)
-    pg = sum(np.abs(O.bf16_from_bits(p).astype(np.float64)) for p in group_rows) if group_rows else 0.0
-    k = len(w_tok)
-    lim = 2.0 ** -8 * (np.abs(o) + pg) + 2 * k * 2.0 ** -24 * mag + 2.0 ** -133
-    assert (np.abs(o - exact) <= lim).all()
+_partial = run_partial
+_bound_check = partial_bound_check
 
 
 def _full_check(r, region_rows=0):
     sh = r["sh"]
-    N, T, H, k = sh.N, sh.T, sh.H, sh.k
-    lay = O.layout(r["idx"], sh.E, N, region_rows)
-    comb, out = _partial(r)
-    y = bf16_np(r["y"])
-    comb_o, lead, out_o = O.combine_partial(y, r["idx"], lay, r["w"])
-    got_comb = bf16_np(comb).reshape(N * T * k, H)
-    led = np.zeros(N * T * k, bool)
-    for s in range(N):
-        for t in range(T):
-            for j in np.flatnonzero(lead[s, t]):
-                led[s * T * k + lay.send_pos[s, t, j]] = True
-    assert (got_comb[led] == comb_o[led]).all(), "group rows"
-    assert (got_comb[~led] == FILL).all(), "rows no group leads were written"
-    got_out = bf16_np(out)
-    assert (got_out == out_o).all(), f"out differs at {np.count_nonzero(got_out != out_o)} elements"
-    yv = O.bf16_from_bits(y).astype(np.float64)
-    for s in range(N):
-        for t in range(T):
-            part = lay.em_row[s, t] >= 0
-            rows = np.zeros((k, H))
-            rows[part] = yv[lay.em_row[s, t][part]]
-            grp = [comb_o[s * T * k + lay.send_pos[s, t, j]] for j in np.flatnonzero(lead[s, t])]
-            _bound_check(got_out[s, t], rows, np.where(part, r["w"][s, t], 0.0), grp)
-    return lay, lead
+    lay = O.layout(r["idx"], sh.E, sh.N, region_rows)
+    return lay, check_partial_full(r, lay)
 
 
 def test_tiny_config():

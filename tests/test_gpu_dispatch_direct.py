@@ -20,7 +20,8 @@ from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import check_layout, export_layout, log, run_all  # noqa: E402
+from gpu_harness import (DIRECT_CALLS, check_layout, check_same_as_two_calls, log, run_all,  # noqa: E402
+                         run_direct)
 
 FILL = 0x5A
 
@@ -37,7 +38,7 @@ def _cfg(name, **kw):
     return W.Config(name, seed=zlib.crc32(name.encode()), **kw)
 
 
-CALLS = {"direct": moe.moe_dispatch_direct, "direct_ll": moe.moe_dispatch_direct_ll}
+CALLS = DIRECT_CALLS
 
 
 @pytest.fixture(params=list(CALLS))
@@ -50,34 +51,10 @@ def _fits_ll(T, k):
 
 
 def _direct(r, payload=True, fill=FILL, call="direct", B=None):
-    """The direct dispatch of run_all's inputs into buffers of its own (or B)."""
-    sh = r["sh"]
-    if B is None:
-        B = moe.allocate(sh, "cuda", payload=payload, combine=False, fill_rows=fill)
-    idx_d = torch.from_numpy(np.ascontiguousarray(r["idx"], np.int32)).cuda()
-    CALLS[call](sh, r["x"] if payload else None, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
-    torch.cuda.synchronize()
-    return B
+    return run_direct(r, call, payload, fill, B)
 
 
-def _bits(t):
-    return t.view(torch.int32) if t.dtype == torch.float32 else t
-
-
-def _same_as_two_calls(r, B2):
-    B1 = r["B"]
-    for f in ("send_pos", "exp_off", "row_src", "x_q", "x_s"):
-        a, b = getattr(B1, f), getattr(B2, f)
-        if a is None:
-            assert b is None
-            continue
-        assert torch.equal(_bits(a), _bits(b)), f
-    g1, g2 = export_layout(r), export_layout(dict(r, B=B2))
-    for key in g1:
-        assert (g1[key] == g2[key]).all(), key
-    flags = moe.moe_status(B2.ws)   # read and cleared
-    assert flags == r["flags"]
-    return flags
+_same_as_two_calls = check_same_as_two_calls
 
 
 def _check_oracle(r, B2, lay):
