@@ -5,7 +5,9 @@
 // write per peer and the receive side accumulates them into the output).
 //
 //   k_comb_send          each workgroup streams a contiguous range of
-//                        expert-major rows: comb[row_src[i]] = y[i]
+//                        expert-major rows: comb[row_src[i]] = y[i] (after
+//                        a fixed-region overflow, also zero rows for the
+//                        slots left without a row)
 //   k_comb_recv          each workgroup streams a contiguous range of
 //                        tokens: fp32 sum over slots of w * y, bf16 out
 //   k_comb_pull          the same sum, rows read in place (expert-major)
@@ -31,6 +33,74 @@ constexpr int kCsWaves = kCombSendShape.waves, kCsThreads = kCombSendShape.threa
 constexpr int kCsUnroll = MOE_CS_UNROLL;
 constexpr int kCrWaves = kCombRecvShape.waves, kCrThreads = kCombRecvShape.threads();
 constexpr int kCpThreads = kCopyShape.threads();
+
+// acc = fl(acc + fl(w * y)) in slot order, never fused into an FMA.
+__device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = w * bf16_lo(v[i]);
+    const float p1 = w * bf16_hi(v[i]);
+    acc[2 * i] = acc[2 * i] + p0;
+    acc[2 * i + 1] = acc[2 * i + 1] + p1;
+  }
+}
+
+constexpr int kSlotGroup = 8;
+#ifndef MOE_COMB_PIECES
+#define MOE_COMB_PIECES 2
+#endif
+constexpr int kCombPieces = MOE_COMB_PIECES;   // 1 KB pieces read per slot row per step
+
+// Expert-major row of a slot of source s with expert e and sender position
+// sp, found from the routing tables: the row combine_send would copy back.
+// -1 for a bad id, or a row that a full fixed region dropped.
+__device__ __forceinline__ int em_row_of(const Dims& D, const Ws& W, int s, int e, int sp) {
+  if (e < 0 || e >= D.E || sp < 0 || sp >= D.TK) return -1;
+  const int d = e / D.L, l = e - d * D.L;
+  const int* so = W.send_off + s * (D.E + 1);
+  const int u = sp - so[e];                                                         // index inside (s, e)
+  const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;      // expert-major
+  const int j = region_row(D, s, (so[e] - so[d * D.L]) + u, W.recv_off[d * (D.N + 1) + s]);   // source-major
+  const int p = W.base[d] + i;
+  return (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) ? p : -1;
+}
+
+// With fixed regions that overflowed, a valid slot can be left without an
+// expert-major row (its own index or its source-major row did not fit).  No
+// row_src entry names its comb row, so the copy loop never writes it; this
+// pass writes it as zeros instead, so that the receive half's sum skips the
+// slot exactly (adding w * +0 leaves a float32 sum unchanged, and the sum,
+// starting at +0, never holds -0), as the pulling combine does.  Comb rows
+// at positions no valid slot has are left untouched.  Without an overflow
+// every workgroup returns after reading the region totals.
+template <int WAVES>
+__device__ void zero_dropped_rows(const Dims& D, const Ws& W, uint16_t* __restrict__ comb) {
+  __shared__ int over;
+  if (threadIdx.x == 0) over = 0;
+  __syncthreads();
+  for (int d = threadIdx.x; d < D.N; d += WAVES * kWave)
+    if (W.recv_total[d] > D.R || D.N * D.Ce + W.recv_off[d * (D.N + 1) + D.N] > D.R) atomicOr(&over, 1);
+  __syncthreads();
+  if (!over) return;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int n16 = D.H / 8;
+  int lo, hi;
+  block_range(D.N * D.TK, lo, hi);   // comb rows s*T*k + sender position
+  for (int p0 = lo + wv * kWave; p0 < hi; p0 += WAVES * kWave) {
+    const int pos = p0 + lane;
+    bool drop = false;
+    if (pos < hi) {
+      const int s = pos / D.TK, p = pos - s * D.TK;
+      const int* so = W.send_off + s * (D.E + 1);
+      if (p < so[D.E]) drop = em_row_of(D, W, s, floor_index(so, D.E + 1, p), p) < 0;
+    }
+    for (uint64_t m = __ballot(drop); m; m &= m - 1) {
+      v4u* row = reinterpret_cast<v4u*>(comb + (int64_t)(p0 + __builtin_ctzll(m)) * D.H);
+      for (int c = lane; c < n16; c += kWave) st16(row + c, v4u{0, 0, 0, 0});
+    }
+  }
+}
 
 __global__ __launch_bounds__(kCsThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                            const int* __restrict__ row_src,
@@ -71,74 +141,9 @@ __global__ __launch_bounds__(kCsThreads) void k_comb_send(Dims D, Ws W, const ui
                       reinterpret_cast<const v4u*>(y + (int64_t)sr * D.H), n16, lane);
     }
   }
+  if (D.R) zero_dropped_rows<kCsWaves>(D, W, comb);   // packed regions never overflow
 }
 
-// acc = fl(acc + fl(w * y)) in slot order, never fused into an FMA.
-__device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p0 = w * bf16_lo(v[i]);
-    const float p1 = w * bf16_hi(v[i]);
-    acc[2 * i] = acc[2 * i] + p0;
-    acc[2 * i + 1] = acc[2 * i + 1] + p1;
-  }
-}
-
-constexpr int kSlotGroup = 8;
-#ifndef MOE_COMB_PIECES
-#define MOE_COMB_PIECES 2
-#endif
-constexpr int kCombPieces = MOE_COMB_PIECES;   // 1 KB pieces read per slot row per step
-
-// Expert-major row of a slot of source s with expert e and sender position
-// sp, found from the routing tables: the row combine_send would copy back.
-// -1 for a bad id, or a row that a full fixed region dropped.
-__device__ __forceinline__ int em_row_of(const Dims& D, const Ws& W, int s, int e, int sp) {
-  if (e < 0 || e >= D.E || sp < 0 || sp >= D.TK) return -1;
-  const int d = e / D.L, l = e - d * D.L;
-  const int* so = W.send_off + s * (D.E + 1);
-  const int u = sp - so[e];                                                         // index inside (s, e)
-  const int i = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + u;      // expert-major
-  const int j = region_row(D, s, (so[e] - so[d * D.L]) + u, W.recv_off[d * (D.N + 1) + s]);   // source-major
-  const int p = W.base[d] + i;
-  return (u >= 0 && i >= 0 && j >= 0 && (D.R == 0 || (i < D.R && j < D.R)) && p < D.rows) ? p : -1;
-}
-
-// With fixed regions that overflowed, a valid slot can be left without an
-// expert-major row (its own index or its source-major row did not fit).  No
-// row_src entry names its comb row, so k_comb_send never writes it; this
-// kernel writes it as zeros instead, so that the receive half's sum skips
-// the slot exactly (adding w * +0 leaves a float32 sum unchanged, and the
-// sum, starting at +0, never holds -0), as the pulling combine does.  Comb
-// rows at positions no valid slot has are left untouched.  Without an
-// overflow every workgroup returns after reading the region totals.
-__global__ __launch_bounds__(kThreads) void k_comb_zero_dropped(Dims D, Ws W, uint16_t* __restrict__ comb) {
-  __shared__ int over;
-  if (threadIdx.x == 0) over = 0;
-  __syncthreads();
-  for (int d = threadIdx.x; d < D.N; d += kThreads)
-    if (W.recv_total[d] > D.R || D.N * D.Ce + W.recv_off[d * (D.N + 1) + D.N] > D.R) atomicOr(&over, 1);
-  __syncthreads();
-  if (!over) return;
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int n16 = D.H / 8;
-  int lo, hi;
-  block_range(D.N * D.TK, lo, hi);   // comb rows s*T*k + sender position
-  for (int p0 = lo + wv * kWave; p0 < hi; p0 += kWavesPerBlock * kWave) {
-    const int pos = p0 + lane;
-    bool drop = false;
-    if (pos < hi) {
-      const int s = pos / D.TK, p = pos - s * D.TK;
-      const int* so = W.send_off + s * (D.E + 1);
-      if (p < so[D.E]) drop = em_row_of(D, W, s, floor_index(so, D.E + 1, p), p) < 0;
-    }
-    for (uint64_t m = __ballot(drop); m; m &= m - 1) {
-      v4u* row = reinterpret_cast<v4u*>(comb + (int64_t)(p0 + __builtin_ctzll(m)) * D.H);
-      for (int c = lane; c < n16; c += kWave) st16(row + c, v4u{0, 0, 0, 0});
-    }
-  }
-}
 
 // Per lane j < k: whether slot j leads its group, i.e. has a row (dest >= 0)
 // and no earlier slot of the token has a row on the same rank.
@@ -407,11 +412,7 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
   const int grid = stream_grid(kCombSendShape, cus, (int64_t)D.rows, kCsWaves);
-  const int rc = launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
-  if (rc || D.R == 0) return rc;   // packed regions never overflow
-  const int64_t need = ((int64_t)D.N * D.TK + kThreads - 1) / kThreads;
-  const int zgrid = (int)(need < (int64_t)cus * 4 ? need : (int64_t)cus * 4);
-  return launch("k_comb_zero_dropped", k_comb_zero_dropped, dim3(zgrid), dim3(kThreads), 0, st, D, W, comb);
+  return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
