@@ -204,15 +204,16 @@ def main():
     total = sum(nbytes[p] for p in PHASES)
 
     # The same step captured once in a HIP graph and replayed (no launch gaps).
-    def graph_ms(send):
+    def graph_ms(send=None, fn=None):
+        fn = fn or (lambda: step(send=send))
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            step(send=send)
+            fn()
         stream.wait_stream(cap)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(send=send)
+            fn()
         torch.cuda.synchronize()
         graph.replay()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -416,7 +417,8 @@ def main():
                 "us": {n: round(v * 1e3, 1) for n, v in zip(
                     ("dispatch_direct", None, "combine_pull") if send_f is None else
                     ("dispatch_send", "dispatch_recv", "combine_pull"), ms_f.mean(axis=0)) if n},
-                "step_us": round(wall_f * 1e6 / args.steps, 1)}
+                "step_us": round(wall_f * 1e6 / args.steps, 1),
+                "graph_step_us": round(graph_ms(fn=step_f) * 1e3, 1)}
         if Bf is not B:
             flags_f = moe.moe_status(Bf.ws)
             if flags_f:
