@@ -787,41 +787,87 @@ constexpr LaunchShape kUnpackLarge = {8, 2};
 constexpr int kUnpackLargeUnroll = 32;
 constexpr int64_t kUnpackLargeRows = 131072;   // rows from which the large form is used
 
+// Staging of one region's routing tables in LDS (k_unpack): the searches
+// that map an expert-major row to its segment then read no global memory.
+#ifndef MOE_UNPACK_STAGE
+#define MOE_UNPACK_STAGE 1
+#endif
+constexpr int kStageInts = 2 * kMaxE + (kMaxE + kMaxN) + (kMaxE + 1) + (kMaxN + 1);
+
 template <int WAVES, int UNROLL>
 __global__ __launch_bounds__(WAVES * kWave) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
                                                        const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
                                                        float* __restrict__ x_s, int* __restrict__ exp_off,
                                                        int* __restrict__ row_src) {
+  constexpr int kT = WAVES * kWave;
   __shared__ int svp[kMaxN + 1];
-  for (int i = threadIdx.x; i <= D.N; i += (WAVES * kWave)) svp[i] = W.vprefix[i];
+  for (int i = threadIdx.x; i <= D.N; i += kT) svp[i] = W.vprefix[i];
   if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += (WAVES * kWave)) exp_off[i] = W.exp_off[i];
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kT) exp_off[i] = W.exp_off[i];
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int N = D.N, E = D.E, L = D.L;
   const bool scales16 = (D.NB & 3) == 0;   // scale rows are whole 16-byte units
   int lo, hi;
   block_range(svp[N], lo, hi);        // valid rows, in region order
+#if MOE_UNPACK_STAGE
+  // Region d0 of the workgroup's first row (normally its only one):
+  //   s_sie[s][l] = src_in_exp[s][d0*L + l], s in [0, N];
+  //   s_so[s][l'] = send_off[s][d0*L + l'], l' in [0, L];
+  //   s_eo[l']    = exp_off[d0][l'];  s_ro[s] = recv_off[d0][s].
+  __shared__ int stage[kStageInts];
+  int* s_sie = stage;
+  int* s_so = s_sie + (N + 1) * L;
+  int* s_eo = s_so + N * (L + 1);
+  int* s_ro = s_eo + (L + 1);
+  const int d0 = lo < hi ? floor_index(svp, N + 1, lo) : -1;
+  if (d0 >= 0) {
+    for (int i = threadIdx.x; i < (N + 1) * L; i += kT) s_sie[i] = W.src_in_exp[(i / L) * E + d0 * L + i % L];
+    for (int i = threadIdx.x; i < N * (L + 1); i += kT)
+      s_so[i] = W.send_off[(i / (L + 1)) * (E + 1) + d0 * L + i % (L + 1)];
+    for (int i = threadIdx.x; i <= L; i += kT) s_eo[i] = W.exp_off[d0 * (L + 1) + i];
+    for (int i = threadIdx.x; i <= N; i += kT) s_ro[i] = W.recv_off[d0 * (N + 1) + i];
+  }
+  __syncthreads();
+#endif
   for (int g0 = lo + wv; g0 < hi; g0 += WAVES * kRowsPerPass) {
     int src = -1, dst = -1;
     const int g = g0 + lane * WAVES;
     if (lane < kRowsPerPass && g < hi) {
       const int d = floor_index(svp, N + 1, g);
       const int i = g - svp[d];                                  // expert-major row inside region d
-      const int* eo = W.exp_off + d * (L + 1);
-      const int l = min(floor_index(eo, L + 1, i), L - 1);
-      const int e = d * L + l;
-      const int u1 = i - eo[l];
-      const int s = min(floor_index(W.src_in_exp + e, N + 1, u1, E), N - 1);
-      const int u = u1 - W.src_in_exp[s * E + e];
-      const int* so = W.send_off + s * (E + 1);
-      const int j = region_row(D, s, (so[e] - so[d * L]) + u, W.recv_off[d * (N + 1) + s]);   // source-major row
+      int s, e, u, sp, sd, ro;   // source, expert, index in (s, e), send_off[s][e], send_off[s][d*L], recv_off[d][s]
+#if MOE_UNPACK_STAGE
+      if (d == d0) {
+        const int l = min(floor_index(s_eo, L + 1, i), L - 1);
+        const int u1 = i - s_eo[l];
+        s = min(floor_index(s_sie + l, N + 1, u1, L), N - 1);
+        e = d * L + l;
+        u = u1 - s_sie[s * L + l];
+        sp = s_so[s * (L + 1) + l];
+        sd = s_so[s * (L + 1)];
+        ro = s_ro[s];
+      } else
+#endif
+      {
+        const int* eo = W.exp_off + d * (L + 1);
+        const int l = min(floor_index(eo, L + 1, i), L - 1);
+        e = d * L + l;
+        const int u1 = i - eo[l];
+        s = min(floor_index(W.src_in_exp + e, N + 1, u1, E), N - 1);
+        u = u1 - W.src_in_exp[s * E + e];
+        const int* so = W.send_off + s * (E + 1);
+        sp = so[e];
+        sd = so[d * L];
+        ro = W.recv_off[d * (N + 1) + s];
+      }
+      const int j = region_row(D, s, (sp - sd) + u, ro);   // source-major row
       const int pd = W.base[d] + i;
       if (pd < D.rows) {
         dst = pd;
         const int ps = W.base[d] + j;
         const bool ok = (D.R == 0 || j < D.R) && j >= 0 && ps < D.rows;
-        row_src[pd] = ok ? s * D.TK + so[e] + u : -1;
+        row_src[pd] = ok ? s * D.TK + sp + u : -1;
         if (ok) src = ps;
       }
     }
