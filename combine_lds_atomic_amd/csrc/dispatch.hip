@@ -160,6 +160,26 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
   pack_scales(D, h0, h1, row, lane, recv_s, ssw);
 }
 
+// MOE_PACK_PRELOAD: k_pack issues a work item's first token loads before it
+// resolves the item's rows, so the two latencies overlap.  Measured in one
+// process: 2-3 us less at the decode shape, no change from combine-heavy
+// size up (where the kernel runs at 98 VGPRs, 4 workgroups per CU, against
+// 65 VGPRs and 7 without it).  Staging the routing tables in LDS as the
+// unpack does changed nothing here and was left out.
+// Minimum waves per SIMD the pack kernels are compiled for (0: the
+// compiler's choice).
+#ifndef MOE_PACK_WAVES_PER_EU
+#define MOE_PACK_WAVES_PER_EU 0
+#endif
+#if MOE_PACK_WAVES_PER_EU
+#define MOE_PACK_BOUNDS __launch_bounds__(kPkThreads, MOE_PACK_WAVES_PER_EU)
+#else
+#define MOE_PACK_BOUNDS __launch_bounds__(kPkThreads)
+#endif
+#ifndef MOE_PACK_PRELOAD
+#define MOE_PACK_PRELOAD 1
+#endif
+
 // The pack loop.  DIRECT = false: rows go to the source-major receive
 // regions (recv_q, recv_s).  DIRECT = true: they go straight to their
 // expert-major rows (x_q, x_s), and the loop also writes row_src and
@@ -180,6 +200,10 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
     int tok, sl, h0, h1;
     item_cols(D, item, tok, sl, h0, h1);
     const int s = tok / D.T, t = tok - s * D.T;
+#if MOE_PACK_PRELOAD
+    v4u a[kPackPasses], b[kPackPasses];
+    if (x != nullptr) load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
+#endif
     // Lane j < k resolves slot j.  With one routing chunk per rank the count
     // kernel already wrote the final position; otherwise it left the rank
     // inside the chunk, and the chunk's base for the expert completes it.
@@ -198,18 +222,18 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
         }
         const int d = e / D.L;
         const int* so = W.send_off + s * (D.E + 1);
+        const int bd = W.base[d];
         const int r = region_row(D, s, sp - so[d * D.L], W.recv_off[d * (D.N + 1) + s]);   // source-major
         if (!DIRECT) {
-          const int pr = W.base[d] + r;
+          const int pr = bd + r;
           if ((D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
         } else {
           // Expert-major row: the same index k_unpack derives, and the same
           // rule: it exists if both it and its source-major row fit.
-          const int l = e - d * D.L;
-          const int ie = W.exp_off[d * (D.L + 1) + l] + W.src_in_exp[s * D.E + e] + (sp - so[e]);
-          const int pe = W.base[d] + ie;
+          const int ie = W.exp_off[d * (D.L + 1) + (e - d * D.L)] + W.src_in_exp[s * D.E + e] + (sp - so[e]);
+          const int pe = bd + ie;
           if ((D.R == 0 || ie < D.R) && ie >= 0 && pe < D.rows) {
-            const bool fits = (D.R == 0 || r < D.R) && r >= 0 && W.base[d] + r < D.rows;
+            const bool fits = (D.R == 0 || r < D.R) && r >= 0 && bd + r < D.rows;
             if (sl == 0) row_src[pe] = fits ? s * D.TK + sp : -1;
             if (fits) row = pe;
           }
@@ -219,17 +243,21 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
       }
     }
     if (x == nullptr) continue;
+#if MOE_PACK_PRELOAD
+    pack_item<true>(D, item, row, x, recv_q, recv_s, sscale[wv], a, b);
+#else
     pack_item<false>(D, item, row, x, recv_q, recv_s, sscale[wv]);
+#endif
   }
 }
 
-__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
+__global__ MOE_PACK_BOUNDS void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                      const int* __restrict__ idx, int* __restrict__ send_pos,
                                                      uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
   pack_tokens<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
 }
 
-__global__ __launch_bounds__(kPkThreads) void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
+__global__ MOE_PACK_BOUNDS void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                             const int* __restrict__ idx, int* __restrict__ send_pos,
                                                             uint8_t* __restrict__ x_q, float* __restrict__ x_s,
                                                             int* __restrict__ row_src, int* __restrict__ exp_off) {
