@@ -350,6 +350,26 @@ def main():
     part_diff = float((out_p.view(torch.int16) != Bc.out.view(torch.int16)).float().mean().item())
     del comb_p
 
+    # Cold-cache phase times (secondary): before each phase call, 1 GiB of
+    # scratch is written so that nothing of the previous phase's output (nor
+    # of this phase's inputs) is left in the 256 MB Infinity Cache.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    calls = [lambda: moe.moe_dispatch_send(sh, x, idx_d, B.recv_q, B.recv_s, B.send_pos, B.ws),
+             lambda: moe.moe_dispatch_recv(sh, B.recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src),
+             lambda: moe.moe_combine_send(shc, y, Bc.row_src, Bc.ws, Bc.comb),
+             lambda: moe.moe_combine_recv(shc, Bc.comb, Bc.send_pos, wc_d, Bc.out)]
+    cold = np.zeros((args.steps, 4))
+    for i in range(args.steps):
+        for p, fn in enumerate(calls):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold[i, p] = e0.elapsed_time(e1)
+    del scratch
+
     # Achievable read+write rate: a plain copy of the dominant phase's bytes.
     dom = max(range(4), key=lambda p: per_phase_ms[p])
     copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
@@ -466,9 +486,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.note}; packed receive regions", "N": cfg.N, "T": T, "T_comb": Tc,
-                   "H": cfg.H, "E": cfg.E, "k": cfg.k, "region_rows": 0, "batch": batch,
+                   "H": cfg.H, "E": cfg.E, "k": cfg.k, "region_rows": 0, "batch": batch, "seed": cfg.seed,
                    "payload": "bf16 in, e4m3fn+fp32 block-128 scales dispatched, bf16 combined with fp32 accumulation"},
         "phases": phase_info,
+        "phases_cold_cache": {name: {"median_us": round(float(np.median(cold[:, p])) * 1e3, 1),
+                                     "p90_us": round(float(np.percentile(cold[:, p], 90)) * 1e3, 1)}
+                              for p, name in enumerate(PHASES)},
         "dispatch_us": round((per_phase_ms[0] + per_phase_ms[1]) * 1e3, 1),
         "combine_us": round((per_phase_ms[2] + per_phase_ms[3]) * 1e3, 1),
         "dispatch_frac": round((nbytes["dispatch_send"] + nbytes["dispatch_recv"]) /
