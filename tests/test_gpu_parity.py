@@ -171,6 +171,21 @@ def test_bad_ids_are_dropped_and_flagged():
     check_full(r, lay)
 
 
+@pytest.mark.parametrize("tight", [False, True])
+def test_many_rows_short_rows(tight):
+    """More than 131072 expert-major rows with short rows: the size from
+    which the row kernels switch to their large-problem forms, every element
+    checked (with tight fixed regions, the overflow path of those forms)."""
+    cfg = _small("many_rows", N=8, T=2100, H=256, E=64, k=8)
+    idx, w = W.routing(cfg, 2100)
+    R = int(O.layout(idx, cfg.E, cfg.N).recv_total.max()) - 40 if tight else 0
+    r = run_all(cfg, 2100, R, idx=idx, w=w)
+    lay = O.layout(idx, cfg.E, cfg.N, R)
+    assert r["B"].rows >= 131072
+    assert bool(r["flags"] & O.FLAG_OVERFLOW) == tight
+    check_full(r, lay)
+
+
 def test_bad_ids_with_several_routing_chunks():
     """T*k > 4096: positions come from chunk bases, and a dropped slot's
     send_pos is still -1."""
