@@ -4,10 +4,13 @@
 // routing is already known from dispatch, rows go back with one contiguous
 // write per peer and the receive side accumulates them into the output).
 //
-//   k_comb_send          each workgroup streams a contiguous range of
-//                        expert-major rows: comb[row_src[i]] = y[i] (after
-//                        a fixed-region overflow, also zero rows for the
-//                        slots left without a row)
+//   k_comb_send          comb[row_src[i]] = y[i] (after a fixed-region
+//                        overflow, also zero rows for the slots left without
+//                        a row): one 1024-thread workgroup per CU copies its
+//                        range of expert-major rows as one flat range of
+//                        16-byte units, thread-interleaved
+//   k_comb_send_rows     the same with one wave per row (problems below
+//                        131072 rows)
 //   k_comb_recv          each workgroup streams a contiguous range of
 //                        tokens: fp32 sum over slots of w * y, bf16 out
 //   k_comb_pull          the same sum, rows read in place (expert-major)
@@ -102,7 +105,7 @@ __device__ void zero_dropped_rows(const Dims& D, const Ws& W, uint16_t* __restri
   }
 }
 
-__global__ __launch_bounds__(kCsThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kCsThreads) void k_comb_send_rows(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                            const int* __restrict__ row_src,
                                                            uint16_t* __restrict__ comb) {
   __shared__ int svp[kMaxN + 1];
@@ -150,10 +153,10 @@ __global__ __launch_bounds__(kCsThreads) void k_comb_send(Dims D, Ws W, const ui
 // before stores), each to its row's comb position.  This is the access
 // pattern of the plain copy; a copy probe with one wave per row ran 4%
 // slower than it on the same data.  Measured in one process, alternating
-// calls: 5% faster than k_comb_send from combine-heavy size up (prefill 6%,
+// calls: 5% faster than k_comb_send_rows from combine-heavy size up (prefill 6%,
 // Kimi 4%), 7% slower at the decode shape; hence the switch by row count.
 constexpr int kCcThreads = 1024, kCcUnroll = 16;
-__global__ __launch_bounds__(kCcThreads) void k_comb_send_coop(Dims D, Ws W, const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kCcThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                const int* __restrict__ row_src,
                                                                uint16_t* __restrict__ comb) {
   __shared__ int svp[kMaxN + 1];
@@ -492,10 +495,10 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
   if (MOE_CS_COOP && (int64_t)D.rows >= kCcMinRows) {
     const int64_t need = ((int64_t)D.rows * (D.H / 8) + kCcThreads * kCcUnroll - 1) / (kCcThreads * kCcUnroll);
     const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
-    return launch("k_comb_send", k_comb_send_coop, dim3(grid), dim3(kCcThreads), 0, st, D, W, y, row_src, comb);
+    return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCcThreads), 0, st, D, W, y, row_src, comb);
   }
   const int grid = stream_grid(kCombSendShape, cus, (int64_t)D.rows, kCsWaves);
-  return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
+  return launch("k_comb_send_rows", k_comb_send_rows, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,

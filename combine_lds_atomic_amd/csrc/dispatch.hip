@@ -10,7 +10,10 @@
 //   k_unpack  each workgroup streams a contiguous range of expert-major rows:
 //             the receive side finds each row's (expert, source) segment from
 //             the exchanged counts alone and copies it out of the
-//             source-major receive region.
+//             source-major receive region; one 1024-thread workgroup per CU,
+//             its rows copied as one thread-interleaved range of 16-byte
+//             units.  k_unpack_rows: the same with one wave per row
+//             (problems below 131072 rows).
 //   k_pack_direct  k_pack storing each row at its expert-major row instead
 //             (peers mapped into each other's memory push straight into the
 //             grouped-GEMM layout; on one GPU every rank is such a peer), so
@@ -805,100 +808,119 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll_direct(Dims D, Ws W, c
 }
 
 constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
-// Unpack launch forms (waves per workgroup x workgroups per CU, 16-B loads per
-// lane issued together while copying a row).  Measured in one process: the
-// large form is 2-4% faster from combine-heavy size up, 4% slower at the
-// decode shapes, where the small one stays.
+// k_unpack_rows launch forms (waves per workgroup x workgroups per CU, 16-B
+// loads per lane issued together while copying a row).  Below
+// kUnpackLargeRows the small form runs.  From there the cooperative k_unpack
+// runs; the large per-row form (2-4% faster than the small one there, 4%
+// slower at the decode shapes) remains for builds with MOE_UNPACK_COOP=0.
 constexpr LaunchShape kUnpackSmall = MOE_UNPACK_SHAPE;
 constexpr int kUnpackSmallUnroll = 8;
 constexpr LaunchShape kUnpackLarge = {8, 2};
 constexpr int kUnpackLargeUnroll = 32;
 constexpr int64_t kUnpackLargeRows = 131072;   // rows from which the large form is used
 
-// Staging of one region's routing tables in LDS (k_unpack): the searches
+// Staging of one region's routing tables in LDS (the unpack kernels): the searches
 // that map an expert-major row to its segment then read no global memory.
 #ifndef MOE_UNPACK_STAGE
 #define MOE_UNPACK_STAGE 1
 #endif
 constexpr int kStageInts = 2 * kMaxE + (kMaxE + kMaxN) + (kMaxE + 1) + (kMaxN + 1);
 
+// One region's routing tables staged in LDS, for the row searches.
+struct UnpackStage {
+  int d0;                      // the region (-1: none staged)
+  int *sie, *so, *eo, *ro;     // src_in_exp / send_off columns, exp_off, recv_off of region d0
+};
+
+// Region d0 of the workgroup's first row lo (normally its only one):
+//   sie[s][l] = src_in_exp[s][d0*L + l], s in [0, N];
+//   so[s][l'] = send_off[s][d0*L + l'], l' in [0, L];
+//   eo[l']    = exp_off[d0][l'];  ro[s] = recv_off[d0][s].
+// Ends with a workgroup barrier.
+template <int THREADS>
+__device__ __forceinline__ UnpackStage unpack_stage(const Dims& D, const Ws& W, const int* svp, int* stage, int lo,
+                                                    int hi) {
+  const int N = D.N, E = D.E, L = D.L;
+  UnpackStage S;
+  S.sie = stage;
+  S.so = S.sie + (N + 1) * L;
+  S.eo = S.so + N * (L + 1);
+  S.ro = S.eo + (L + 1);
+  S.d0 = MOE_UNPACK_STAGE && lo < hi ? floor_index(svp, N + 1, lo) : -1;
+  if (S.d0 >= 0) {
+    const int d0 = S.d0;
+    for (int i = threadIdx.x; i < (N + 1) * L; i += THREADS) S.sie[i] = W.src_in_exp[(i / L) * E + d0 * L + i % L];
+    for (int i = threadIdx.x; i < N * (L + 1); i += THREADS)
+      S.so[i] = W.send_off[(i / (L + 1)) * (E + 1) + d0 * L + i % (L + 1)];
+    for (int i = threadIdx.x; i <= L; i += THREADS) S.eo[i] = W.exp_off[d0 * (L + 1) + i];
+    for (int i = threadIdx.x; i <= N; i += THREADS) S.ro[i] = W.recv_off[d0 * (N + 1) + i];
+  }
+  __syncthreads();
+  return S;
+}
+
+// Valid row g (region order): its physical expert-major row dst and the
+// source-major row src it copies (-1: none; an expert-major row whose
+// source-major row was dropped gets dst with src -1).  Writes row_src[dst].
+__device__ __forceinline__ void unpack_row(const Dims& D, const Ws& W, const UnpackStage& S, const int* svp, int g,
+                                           int* __restrict__ row_src, int& src, int& dst) {
+  const int N = D.N, E = D.E, L = D.L;
+  src = dst = -1;
+  const int d = floor_index(svp, N + 1, g);
+  const int i = g - svp[d];                                  // expert-major row inside region d
+  int s, u, sp, sd, ro;   // source, index in (s, e), send_off[s][e], send_off[s][d*L], recv_off[d][s]
+  if (d == S.d0) {
+    const int l = min(floor_index(S.eo, L + 1, i), L - 1);
+    const int u1 = i - S.eo[l];
+    s = min(floor_index(S.sie + l, N + 1, u1, L), N - 1);
+    u = u1 - S.sie[s * L + l];
+    sp = S.so[s * (L + 1) + l];
+    sd = S.so[s * (L + 1)];
+    ro = S.ro[s];
+  } else {
+    const int* eo = W.exp_off + d * (L + 1);
+    const int l = min(floor_index(eo, L + 1, i), L - 1);
+    const int e = d * L + l;
+    const int u1 = i - eo[l];
+    s = min(floor_index(W.src_in_exp + e, N + 1, u1, E), N - 1);
+    u = u1 - W.src_in_exp[s * E + e];
+    const int* so = W.send_off + s * (E + 1);
+    sp = so[e];
+    sd = so[d * L];
+    ro = W.recv_off[d * (N + 1) + s];
+  }
+  const int j = region_row(D, s, (sp - sd) + u, ro);   // source-major row
+  const int pd = W.base[d] + i;
+  if (pd < D.rows) {
+    dst = pd;
+    const int ps = W.base[d] + j;
+    const bool ok = (D.R == 0 || j < D.R) && j >= 0 && ps < D.rows;
+    row_src[pd] = ok ? s * D.TK + sp + u : -1;
+    if (ok) src = ps;
+  }
+}
+
 template <int WAVES, int UNROLL>
-__global__ __launch_bounds__(WAVES * kWave) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
+__global__ __launch_bounds__(WAVES * kWave) void k_unpack_rows(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
                                                        const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
                                                        float* __restrict__ x_s, int* __restrict__ exp_off,
                                                        int* __restrict__ row_src) {
   constexpr int kT = WAVES * kWave;
   __shared__ int svp[kMaxN + 1];
+  __shared__ int stage[kStageInts];
   for (int i = threadIdx.x; i <= D.N; i += kT) svp[i] = W.vprefix[i];
   if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
     for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kT) exp_off[i] = W.exp_off[i];
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int N = D.N, E = D.E, L = D.L;
   const bool scales16 = (D.NB & 3) == 0;   // scale rows are whole 16-byte units
   int lo, hi;
-  block_range(svp[N], lo, hi);        // valid rows, in region order
-#if MOE_UNPACK_STAGE
-  // Region d0 of the workgroup's first row (normally its only one):
-  //   s_sie[s][l] = src_in_exp[s][d0*L + l], s in [0, N];
-  //   s_so[s][l'] = send_off[s][d0*L + l'], l' in [0, L];
-  //   s_eo[l']    = exp_off[d0][l'];  s_ro[s] = recv_off[d0][s].
-  __shared__ int stage[kStageInts];
-  int* s_sie = stage;
-  int* s_so = s_sie + (N + 1) * L;
-  int* s_eo = s_so + N * (L + 1);
-  int* s_ro = s_eo + (L + 1);
-  const int d0 = lo < hi ? floor_index(svp, N + 1, lo) : -1;
-  if (d0 >= 0) {
-    for (int i = threadIdx.x; i < (N + 1) * L; i += kT) s_sie[i] = W.src_in_exp[(i / L) * E + d0 * L + i % L];
-    for (int i = threadIdx.x; i < N * (L + 1); i += kT)
-      s_so[i] = W.send_off[(i / (L + 1)) * (E + 1) + d0 * L + i % (L + 1)];
-    for (int i = threadIdx.x; i <= L; i += kT) s_eo[i] = W.exp_off[d0 * (L + 1) + i];
-    for (int i = threadIdx.x; i <= N; i += kT) s_ro[i] = W.recv_off[d0 * (N + 1) + i];
-  }
-  __syncthreads();
-#endif
+  block_range(svp[D.N], lo, hi);        // valid rows, in region order
+  const UnpackStage S = unpack_stage<kT>(D, W, svp, stage, lo, hi);
   for (int g0 = lo + wv; g0 < hi; g0 += WAVES * kRowsPerPass) {
     int src = -1, dst = -1;
     const int g = g0 + lane * WAVES;
-    if (lane < kRowsPerPass && g < hi) {
-      const int d = floor_index(svp, N + 1, g);
-      const int i = g - svp[d];                                  // expert-major row inside region d
-      int s, e, u, sp, sd, ro;   // source, expert, index in (s, e), send_off[s][e], send_off[s][d*L], recv_off[d][s]
-#if MOE_UNPACK_STAGE
-      if (d == d0) {
-        const int l = min(floor_index(s_eo, L + 1, i), L - 1);
-        const int u1 = i - s_eo[l];
-        s = min(floor_index(s_sie + l, N + 1, u1, L), N - 1);
-        e = d * L + l;
-        u = u1 - s_sie[s * L + l];
-        sp = s_so[s * (L + 1) + l];
-        sd = s_so[s * (L + 1)];
-        ro = s_ro[s];
-      } else
-#endif
-      {
-        const int* eo = W.exp_off + d * (L + 1);
-        const int l = min(floor_index(eo, L + 1, i), L - 1);
-        e = d * L + l;
-        const int u1 = i - eo[l];
-        s = min(floor_index(W.src_in_exp + e, N + 1, u1, E), N - 1);
-        u = u1 - W.src_in_exp[s * E + e];
-        const int* so = W.send_off + s * (E + 1);
-        sp = so[e];
-        sd = so[d * L];
-        ro = W.recv_off[d * (N + 1) + s];
-      }
-      const int j = region_row(D, s, (sp - sd) + u, ro);   // source-major row
-      const int pd = W.base[d] + i;
-      if (pd < D.rows) {
-        dst = pd;
-        const int ps = W.base[d] + j;
-        const bool ok = (D.R == 0 || j < D.R) && j >= 0 && ps < D.rows;
-        row_src[pd] = ok ? s * D.TK + sp + u : -1;
-        if (ok) src = ps;
-      }
-    }
+    if (lane < kRowsPerPass && g < hi) unpack_row(D, W, S, svp, g, row_src, src, dst);
     if (x_q == nullptr) continue;   // layout only
     for (int r = 0; r < kRowsPerPass; ++r) {
       const int sr = __builtin_amdgcn_readlane(src, r);
@@ -918,6 +940,94 @@ __global__ __launch_bounds__(WAVES * kWave) void k_unpack(Dims D, Ws W, const ui
         for (int c = lane; c < D.NB; c += kWave) x_s[(int64_t)dr * D.NB + c] = recv_s[(int64_t)sr * D.NB + c];
       }
     }
+  }
+}
+
+// The same unpack with the whole workgroup on consecutive rows (the access
+// pattern of the plain copy, as k_comb_send): per chunk of rows, their
+// sources are resolved into LDS, then thread t copies the chunk's 16-byte
+// payload units t, t + kUcThreads, ... (kUcUnroll per step, loads before
+// stores) and its scale units likewise.  Measured in one process,
+// alternating calls, against the per-row large form: combine-heavy 1307-1402
+// against 1403-1461 us, prefill 2633-2697 against 2776-2840.  (Sixteen
+// units per thread would spill at this workgroup size.)
+constexpr int kUcThreads = 1024, kUcUnroll = 8;
+constexpr int kUcMaxRows = kUcThreads * kUcUnroll / (kScaleBlock / 16);   // rows per chunk at H = 128
+__global__ __launch_bounds__(kUcThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
+                                                            const float* __restrict__ recv_s,
+                                                            uint8_t* __restrict__ x_q, float* __restrict__ x_s,
+                                                            int* __restrict__ exp_off, int* __restrict__ row_src) {
+  __shared__ int svp[kMaxN + 1];
+  __shared__ int stage[kStageInts];
+  __shared__ int t_src[kUcMaxRows], t_dst[kUcMaxRows];
+  for (int i = threadIdx.x; i <= D.N; i += kUcThreads) svp[i] = W.vprefix[i];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kUcThreads) exp_off[i] = W.exp_off[i];
+  __syncthreads();
+  int lo, hi;
+  block_range(svp[D.N], lo, hi);
+  const UnpackStage S = unpack_stage<kUcThreads>(D, W, svp, stage, lo, hi);
+  const int n16 = D.H / 16;                                    // payload units per row
+  const int rchunk = kUcThreads * kUcUnroll / n16;             // whole rows per chunk (n16 >= 8)
+  const int dr1 = kUcThreads / n16, dc1 = kUcThreads % n16;   // per-slot advance of (row, column)
+  const int r0 = threadIdx.x / n16, c0 = threadIdx.x % n16;
+  const v4u* __restrict__ qs = reinterpret_cast<const v4u*>(recv_q);
+  v4u* __restrict__ qd = reinterpret_cast<v4u*>(x_q);
+  const bool scales16 = (D.NB & 3) == 0;
+  for (int g0 = lo; g0 < hi; g0 += rchunk) {
+    const int nr = min(rchunk, hi - g0);
+    for (int r = threadIdx.x; r < nr; r += kUcThreads) {
+      int src, dst;
+      unpack_row(D, W, S, svp, g0 + r, row_src, src, dst);
+      t_src[r] = dst >= 0 ? src : -1;
+      t_dst[r] = dst;
+    }
+    __syncthreads();
+    if (x_q != nullptr) {
+      v4u v[kUcUnroll];
+      int dst[kUcUnroll];
+      int r = r0, c = c0;
+#pragma unroll
+      for (int u = 0; u < kUcUnroll; ++u) {
+        dst[u] = -1;
+        if (r < nr) {
+          const int sr = t_src[r];
+          if (sr >= 0) {
+            dst[u] = t_dst[r];
+            v[u] = ld16(qs + (int64_t)sr * n16 + c);
+          }
+        }
+        r += dr1;
+        c += dc1;
+        if (c >= n16) {
+          c -= n16;
+          ++r;
+        }
+      }
+      c = c0;
+#pragma unroll
+      for (int u = 0; u < kUcUnroll; ++u) {
+        if (dst[u] >= 0) st16(qd + (int64_t)dst[u] * n16 + c, v[u]);
+        c += dc1;
+        if (c >= n16) c -= n16;
+      }
+      // Scales: NB floats per row, as 16-byte units where rows are whole units.
+      if (scales16) {
+        const int s16 = D.NB / 4;
+        for (int f = threadIdx.x; f < nr * s16; f += kUcThreads) {
+          const int rr = f / s16, cc = f - rr * s16;
+          if (t_src[rr] >= 0)
+            st16(reinterpret_cast<v4u*>(x_s + (int64_t)t_dst[rr] * D.NB) + cc,
+                 ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)t_src[rr] * D.NB) + cc));
+        }
+      } else {
+        for (int f = threadIdx.x; f < nr * D.NB; f += kUcThreads) {
+          const int rr = f / D.NB, cc = f - rr * D.NB;
+          if (t_src[rr] >= 0) x_s[(int64_t)t_dst[rr] * D.NB + cc] = recv_s[(int64_t)t_src[rr] * D.NB + cc];
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -946,17 +1056,27 @@ int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, 
   return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
 }
 
+#ifndef MOE_UNPACK_COOP
+#define MOE_UNPACK_COOP 1
+#endif
+
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
+  if (MOE_UNPACK_COOP && (int64_t)D.rows >= kUnpackLargeRows) {
+    const int64_t need = ((int64_t)D.rows * (D.H / 16) + kUcThreads * kUcUnroll - 1) / (kUcThreads * kUcUnroll);
+    const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
+    return launch("k_unpack", k_unpack, dim3(grid), dim3(kUcThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s,
+                  exp_off, row_src);
+  }
   if ((int64_t)D.rows >= kUnpackLargeRows) {
     constexpr LaunchShape S = kUnpackLarge;
     const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
-    return launch("k_unpack", k_unpack<S.waves, kUnpackLargeUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
+    return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackLargeUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
                   recv_q, recv_s, x_q, x_s, exp_off, row_src);
   }
   constexpr LaunchShape S = kUnpackSmall;
   const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
-  return launch("k_unpack", k_unpack<S.waves, kUnpackSmallUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
+  return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackSmallUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
                 recv_q, recv_s, x_q, x_s, exp_off, row_src);
 }
 
