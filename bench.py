@@ -38,14 +38,20 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 PHASES = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
 KERNEL_OF = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
              "combine_recv": "k_comb_recv"}
-# Below this many rows the library runs the one-wave-per-row forms of the
-# unpack and of combine send (k_unpack_rows, k_comb_send_rows).
+# The library's small-problem forms: one wave per row below 131072 rows
+# (k_unpack_rows, k_comb_send_rows), one wave per token below 16384 tokens
+# (k_comb_recv_tokens).
 ROWS_FORM_BELOW = 131072
+TOKENS_FORM_BELOW = 16384
 
 
-def kernel_of(phase: str, rows: int) -> str:
+def kernel_of(phase: str, rows: int, tokens: int) -> str:
     k = KERNEL_OF[phase]
-    return k + "_rows" if phase in ("dispatch_recv", "combine_send") and rows < ROWS_FORM_BELOW else k
+    if phase in ("dispatch_recv", "combine_send") and rows < ROWS_FORM_BELOW:
+        return k + "_rows"
+    if phase == "combine_recv" and tokens < TOKENS_FORM_BELOW:
+        return k + "_tokens"
+    return k
 
 
 def algorithmic_bytes(N, T, H, E, k, Tc=None, G=None):
@@ -477,7 +483,7 @@ def main():
         single["early_rows"]["dispatch_send"] = info("dispatch_send", early_ms)
     dom_name = PHASES[dom]
     achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
-    kernel = kernel_of(dom_name, B.rows if dom_name.startswith("dispatch") else Bc.rows)
+    kernel = kernel_of(dom_name, B.rows if dom_name.startswith("dispatch") else Bc.rows, cfg.N * Tc)
     value = total / (step_ms * 1e-3) / 1e9
     batch = f"T={T}" if Tc == T else f"dispatch T={T}, combine T={Tc}"
     res = {

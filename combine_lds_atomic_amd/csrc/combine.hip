@@ -12,8 +12,12 @@
 //   k_comb_send_rows     the same with one wave per row (problems below
 //                        131072 rows)
 //   k_comb_recv          each workgroup streams a contiguous range of
-//                        tokens: fp32 sum over slots of w * y, bf16 out
-//   k_comb_pull          the same sum, rows read in place (expert-major)
+//                        tokens: fp32 sum over slots of w * y, bf16 out; one
+//                        1024-thread workgroup per CU, thread-interleaved
+//                        16-byte output units (k_comb_recv_tokens: one wave
+//                        per token, below 16384 tokens)
+//   k_comb_pull          the same sum, rows read in place (expert-major);
+//                        k_comb_pull_tokens below 16384 tokens
 //   k_comb_send_partial  send-side partial sums: one bf16 row per (token,
 //                        destination rank) group ("Evaluation:
 //                        dispatch/combine latency": accumulating on the send
@@ -320,14 +324,14 @@ __device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const
   }
 }
 
-__global__ __launch_bounds__(kCrThreads) void k_comb_recv(Dims D, Ws W, const uint16_t* __restrict__ comb,
+__global__ __launch_bounds__(kCrThreads) void k_comb_recv_tokens(Dims D, Ws W, const uint16_t* __restrict__ comb,
                                                            const int* __restrict__ send_pos,
                                                            const float* __restrict__ topk_w,
                                                            uint16_t* __restrict__ out) {
   combine_tokens<CombMode::kRecv>(D, W, comb, nullptr, send_pos, topk_w, out);
 }
 
-__global__ __launch_bounds__(kCrThreads) void k_comb_pull(Dims D, Ws W, const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kCrThreads) void k_comb_pull_tokens(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                            const int* __restrict__ idx,
                                                            const int* __restrict__ send_pos,
                                                            const float* __restrict__ topk_w,
@@ -350,6 +354,87 @@ __device__ __forceinline__ v4u pack_bf16x8(const float* acc) {
   o[2] = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
   o[3] = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
   return o;
+}
+
+// The receive-side sums with the whole workgroup on a chunk of consecutive
+// tokens (the plain copy's pattern, as k_comb_send): the chunk's slot rows
+// and weights are resolved into LDS, then thread t forms the output's
+// 16-byte units t, t + kCoThreads, ..., each from the same 16 bytes of the
+// token's k slot rows, summed in slot order exactly as combine_tokens does.
+// Measured in one process, alternating calls: 1.5-2% faster than the
+// one-wave-per-token form from combine-heavy size up (1655-1661 against
+// 1683-1691 us; prefill 3300-3318 against 3360-3391), equal at the decode
+// shape, 50% slower at the tiny one; hence the switch by token count.
+// One or two workgroups per CU and 4, 8 or 16 units per thread were within
+// 1% of each other.
+#ifndef MOE_CR_COOP_UNITS
+#define MOE_CR_COOP_UNITS 8
+#endif
+constexpr int kCoThreads = 1024, kCoUnits = MOE_CR_COOP_UNITS, kCoTable = 4096;
+template <CombMode MODE>
+__device__ __forceinline__ void combine_tokens_coop(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
+                                                    const int* __restrict__ idx, const int* __restrict__ send_pos,
+                                                    const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
+  __shared__ int t_row[kCoTable];
+  __shared__ float t_w[kCoTable];
+  const int n16 = D.H / 8, k = D.k;
+  int ntok = kCoThreads * kCoUnits / n16;                 // tokens per chunk
+  ntok = max(1, min(ntok, kCoTable / k));
+  const v4u* __restrict__ rs = reinterpret_cast<const v4u*>(rows);
+  v4u* __restrict__ os = reinterpret_cast<v4u*>(out);
+  int lo, hi;
+  block_range(D.N * D.T, lo, hi);
+  for (int t0 = lo; t0 < hi; t0 += ntok) {
+    const int nt = min(ntok, hi - t0);
+    for (int i = threadIdx.x; i < nt * k; i += kCoThreads) {
+      const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
+      const int s = (t0 + i / k) / D.T;
+      const int sp = send_pos[slot];
+      int row;
+      if (MODE == CombMode::kRecv) row = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
+      else row = em_row_of(D, W, s, idx[slot], sp);
+      t_row[i] = row;
+      t_w[i] = topk_w[slot];
+    }
+    __syncthreads();
+    for (int f = threadIdx.x; f < nt * n16; f += kCoThreads) {
+      const int tt = f / n16, c = f - tt * n16;
+      const int* tr = t_row + tt * k;
+      const float* tw = t_w + tt * k;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+        v4u v[kSlotGroup];
+        int rr[kSlotGroup];
+#pragma unroll
+        for (int jj = 0; jj < kSlotGroup; ++jj) {
+          rr[jj] = j0 + jj < k ? tr[j0 + jj] : -1;
+          v[jj] = rr[jj] >= 0 ? ld16(rs + (int64_t)rr[jj] * n16 + c) : v4u{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int jj = 0; jj < kSlotGroup; ++jj)
+          if (rr[jj] >= 0) acc_row8(acc, tw[j0 + jj], v[jj]);
+      }
+      st16(os + (int64_t)(t0 + tt) * n16 + c, pack_bf16x8(acc));
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kCoThreads) void k_comb_recv(Dims D, Ws W, const uint16_t* __restrict__ comb,
+                                                               const int* __restrict__ send_pos,
+                                                               const float* __restrict__ topk_w,
+                                                               uint16_t* __restrict__ out) {
+  combine_tokens_coop<CombMode::kRecv>(D, W, comb, nullptr, send_pos, topk_w, out);
+}
+
+__global__ __launch_bounds__(kCoThreads) void k_comb_pull(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                               const int* __restrict__ idx,
+                                                               const int* __restrict__ send_pos,
+                                                               const float* __restrict__ topk_w,
+                                                               uint16_t* __restrict__ out) {
+  combine_tokens_coop<CombMode::kPull>(D, W, y, idx, send_pos, topk_w, out);
 }
 
 // Send-side partial sums, token by token (one wave per token): for each
@@ -501,18 +586,37 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
   return launch("k_comb_send_rows", k_comb_send_rows, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
 }
 
+#ifndef MOE_CR_COOP
+#define MOE_CR_COOP 1
+#endif
+#ifndef MOE_CR_COOP_PER_CU
+#define MOE_CR_COOP_PER_CU 1
+#endif
+constexpr int64_t kCoMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
+static int coop_grid(const Dims& D, int cus) {
+  const int64_t need = ((int64_t)D.N * D.T * (D.H / 8) + kCoThreads * kCoUnits - 1) / (kCoThreads * kCoUnits);
+  const int64_t cap = (int64_t)cus * MOE_CR_COOP_PER_CU;
+  return (int)(need < cap ? (need < 1 ? 1 : need) : cap);
+}
+
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
+  if (MOE_CR_COOP && (int64_t)D.N * D.T >= kCoMinTokens)
+    return launch("k_comb_recv", k_comb_recv, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, Ws{}, comb,
+                  send_pos, w, out);
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_recv", k_comb_recv, dim3(grid), dim3(kCrThreads), 0, st, D, Ws{}, comb, send_pos, w, out);
+  return launch("k_comb_recv_tokens", k_comb_recv_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, Ws{}, comb, send_pos, w, out);
 }
 
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
+  if (MOE_CR_COOP && (int64_t)D.N * D.T >= kCoMinTokens)
+    return launch("k_comb_pull", k_comb_pull, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, W, y, idx,
+                  send_pos, w, out);
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_pull", k_comb_pull, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
+  return launch("k_comb_pull_tokens", k_comb_pull_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
 int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
