@@ -183,6 +183,46 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
 #define MOE_PACK_PRELOAD 1
 #endif
 
+// The row slot i (of rank s's T*k) is packed to, -1 for none.  DIRECT =
+// false: its source-major receive row; DIRECT = true: its expert-major row,
+// by the same index and rule k_unpack uses (it exists if both it and its
+// source-major row fit; row_src -1 when only the source-major one does not).
+// With several routing chunks per rank the count kernel left the rank
+// inside the chunk, and the chunk's base for the expert completes it; then
+// the position (or -1 for a dropped slot) is written here, as row_src is in
+// the direct form, when `write` is set.
+template <bool DIRECT>
+__device__ __forceinline__ int pack_slot_row(const Dims& D, const Ws& W, const int* __restrict__ idx,
+                                             int* __restrict__ send_pos, int* __restrict__ row_src, int s, int i,
+                                             bool write) {
+  const int64_t slot = (int64_t)s * D.TK + i;
+  const int e = idx[slot];
+  if (e < 0 || e >= D.E) {
+    if (D.B > 1 && write) send_pos[slot] = -1;   // (the count kernel marks it when it writes positions itself)
+    return -1;
+  }
+  int sp;
+  if (D.B > 1) {
+    sp = W.local[slot] + W.blk[((int64_t)s * D.B + i / D.C) * D.E + e];
+    if (write) send_pos[slot] = sp;
+  } else {
+    sp = send_pos[slot];
+  }
+  const int d = e / D.L;
+  const int* so = W.send_off + s * (D.E + 1);
+  const int bd = W.base[d];
+  const int r = region_row(D, s, sp - so[d * D.L], W.recv_off[d * (D.N + 1) + s]);   // source-major
+  const bool fits = (D.R == 0 || r < D.R) && r >= 0 && bd + r < D.rows;
+  if (!DIRECT) return fits ? bd + r : -1;
+  const int ie = W.exp_off[d * (D.L + 1) + (e - d * D.L)] + W.src_in_exp[s * D.E + e] + (sp - so[e]);
+  const int pe = bd + ie;
+  if ((D.R == 0 || ie < D.R) && ie >= 0 && pe < D.rows) {
+    if (write) row_src[pe] = fits ? s * D.TK + sp : -1;
+    return fits ? pe : -1;
+  }
+  return -1;
+}
+
 // The pack loop.  DIRECT = false: rows go to the source-major receive
 // regions (recv_q, recv_s).  DIRECT = true: they go straight to their
 // expert-major rows (x_q, x_s), and the loop also writes row_src and
@@ -207,44 +247,8 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
     v4u a[kPackPasses], b[kPackPasses];
     if (x != nullptr) load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
 #endif
-    // Lane j < k resolves slot j.  With one routing chunk per rank the count
-    // kernel already wrote the final position; otherwise it left the rank
-    // inside the chunk, and the chunk's base for the expert completes it.
-    int row = -1;
-    if (lane < D.k) {
-      const int i = t * D.k + lane;
-      const int64_t slot = (int64_t)s * D.TK + i;
-      const int e = idx[slot];
-      if (e >= 0 && e < D.E) {
-        int sp;
-        if (D.B > 1) {
-          sp = W.local[slot] + W.blk[((int64_t)s * D.B + i / D.C) * D.E + e];
-          if (sl == 0) send_pos[slot] = sp;
-        } else {
-          sp = send_pos[slot];
-        }
-        const int d = e / D.L;
-        const int* so = W.send_off + s * (D.E + 1);
-        const int bd = W.base[d];
-        const int r = region_row(D, s, sp - so[d * D.L], W.recv_off[d * (D.N + 1) + s]);   // source-major
-        if (!DIRECT) {
-          const int pr = bd + r;
-          if ((D.R == 0 || r < D.R) && r >= 0 && pr < D.rows) row = pr;
-        } else {
-          // Expert-major row: the same index k_unpack derives, and the same
-          // rule: it exists if both it and its source-major row fit.
-          const int ie = W.exp_off[d * (D.L + 1) + (e - d * D.L)] + W.src_in_exp[s * D.E + e] + (sp - so[e]);
-          const int pe = bd + ie;
-          if ((D.R == 0 || ie < D.R) && ie >= 0 && pe < D.rows) {
-            const bool fits = (D.R == 0 || r < D.R) && r >= 0 && bd + r < D.rows;
-            if (sl == 0) row_src[pe] = fits ? s * D.TK + sp : -1;
-            if (fits) row = pe;
-          }
-        }
-      } else if (D.B > 1 && sl == 0) {
-        send_pos[slot] = -1;   // a dropped slot (the count kernel marks it when it writes positions itself)
-      }
-    }
+    // Lane j < k resolves slot j.
+    const int row = lane < D.k ? pack_slot_row<DIRECT>(D, W, idx, send_pos, row_src, s, t * D.k + lane, sl == 0) : -1;
     if (x == nullptr) continue;
 #if MOE_PACK_PRELOAD
     pack_item<true>(D, item, row, x, recv_q, recv_s, sscale[wv], a, b);
