@@ -169,16 +169,6 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
 // size up (where the kernel runs at 98 VGPRs, 4 workgroups per CU, against
 // 65 VGPRs and 7 without it).  Staging the routing tables in LDS as the
 // unpack does changed nothing here and was left out.
-// Minimum waves per SIMD the pack kernels are compiled for (0: the
-// compiler's choice).
-#ifndef MOE_PACK_WAVES_PER_EU
-#define MOE_PACK_WAVES_PER_EU 0
-#endif
-#if MOE_PACK_WAVES_PER_EU
-#define MOE_PACK_BOUNDS __launch_bounds__(kPkThreads, MOE_PACK_WAVES_PER_EU)
-#else
-#define MOE_PACK_BOUNDS __launch_bounds__(kPkThreads)
-#endif
 #ifndef MOE_PACK_PRELOAD
 #define MOE_PACK_PRELOAD 1
 #endif
@@ -258,13 +248,13 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
   }
 }
 
-__global__ MOE_PACK_BOUNDS void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                      const int* __restrict__ idx, int* __restrict__ send_pos,
                                                      uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
   pack_tokens<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
 }
 
-__global__ MOE_PACK_BOUNDS void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kPkThreads) void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                             const int* __restrict__ idx, int* __restrict__ send_pos,
                                                             uint8_t* __restrict__ x_q, float* __restrict__ x_s,
                                                             int* __restrict__ row_src, int* __restrict__ exp_off) {
