@@ -39,7 +39,7 @@ PHASES = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
 KERNEL_OF = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
              "combine_recv": "k_comb_recv"}
 # The library's small-problem forms: one wave per row below 131072 rows
-# (k_unpack_rows, k_comb_send_rows), one wave per token below 16384 tokens
+# (k_comb_send_rows), one wave per token below 16384 tokens
 # (k_comb_recv_tokens).
 ROWS_FORM_BELOW = 131072
 TOKENS_FORM_BELOW = 16384
@@ -47,7 +47,7 @@ TOKENS_FORM_BELOW = 16384
 
 def kernel_of(phase: str, rows: int, tokens: int) -> str:
     k = KERNEL_OF[phase]
-    if phase in ("dispatch_recv", "combine_send") and rows < ROWS_FORM_BELOW:
+    if phase == "combine_send" and rows < ROWS_FORM_BELOW:
         return k + "_rows"
     if phase == "combine_recv" and tokens < TOKENS_FORM_BELOW:
         return k + "_tokens"

@@ -12,8 +12,8 @@
 //             the exchanged counts alone and copies it out of the
 //             source-major receive region; one 1024-thread workgroup per CU,
 //             its rows copied as one thread-interleaved range of 16-byte
-//             units.  k_unpack_rows: the same with one wave per row
-//             (problems below 131072 rows).
+//             units.  (k_unpack_rows, one wave per row, remains for
+//             builds with MOE_UNPACK_COOP=0.)
 //   k_pack_direct  k_pack storing each row at its expert-major row instead
 //             (peers mapped into each other's memory push straight into the
 //             grouped-GEMM layout; on one GPU every rank is such a peer), so
@@ -802,16 +802,13 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll_direct(Dims D, Ws W, c
 }
 
 constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
-// k_unpack_rows launch forms (waves per workgroup x workgroups per CU, 16-B
-// loads per lane issued together while copying a row).  Below
-// kUnpackLargeRows the small form runs.  From there the cooperative k_unpack
-// runs; the large per-row form (2-4% faster than the small one there, 4%
-// slower at the decode shapes) remains for builds with MOE_UNPACK_COOP=0.
-constexpr LaunchShape kUnpackSmall = MOE_UNPACK_SHAPE;
-constexpr int kUnpackSmallUnroll = 8;
-constexpr LaunchShape kUnpackLarge = {8, 2};
-constexpr int kUnpackLargeUnroll = 32;
-constexpr int64_t kUnpackLargeRows = 131072;   // rows from which the large form is used
+// k_unpack_rows launch form (waves per workgroup x workgroups per CU, 16-B
+// loads per lane issued together while copying a row), used only by builds
+// with MOE_UNPACK_COOP=0: the cooperative k_unpack measured equal at the
+// decode shape and faster everywhere else (tiny 21 against 25 us, Kimi
+// dispatch 199-201 against 205-213, combine-heavy and prefill 4-7%).
+constexpr LaunchShape kUnpackRowsShape = MOE_UNPACK_SHAPE;
+constexpr int kUnpackRowsUnroll = 8;
 
 // Staging of one region's routing tables in LDS (the unpack kernels): the searches
 // that map an expert-major row to its segment then read no global memory.
@@ -1056,22 +1053,16 @@ int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, 
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
-  if (MOE_UNPACK_COOP && (int64_t)D.rows >= kUnpackLargeRows) {
+  if (MOE_UNPACK_COOP) {
     const int64_t need = ((int64_t)D.rows * (D.H / 16) + kUcThreads * kUcUnroll - 1) / (kUcThreads * kUcUnroll);
     const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
     return launch("k_unpack", k_unpack, dim3(grid), dim3(kUcThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s,
                   exp_off, row_src);
   }
-  if ((int64_t)D.rows >= kUnpackLargeRows) {
-    constexpr LaunchShape S = kUnpackLarge;
-    const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
-    return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackLargeUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
-                  recv_q, recv_s, x_q, x_s, exp_off, row_src);
-  }
-  constexpr LaunchShape S = kUnpackSmall;
+  constexpr LaunchShape S = kUnpackRowsShape;
   const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
-  return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackSmallUnroll>, dim3(grid), dim3(S.threads()), 0, st, D, W,
-                recv_q, recv_s, x_q, x_s, exp_off, row_src);
+  return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackRowsUnroll>, dim3(grid), dim3(S.threads()), 0, st, D,
+                W, recv_q, recv_s, x_q, x_s, exp_off, row_src);
 }
 
 // Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic
