@@ -159,7 +159,13 @@ __global__ __launch_bounds__(kCsThreads) void k_comb_send_rows(Dims D, Ws W, con
 // slower than it on the same data.  Measured in one process, alternating
 // calls: 5% faster than k_comb_send_rows from combine-heavy size up (prefill 6%,
 // Kimi 4%), 7% slower at the decode shape; hence the switch by row count.
-constexpr int kCcThreads = 1024, kCcUnroll = 16;
+// Each unit's load waits for its row_src: issuing the loads first, with
+// the row_src reads beside them, made this form 5% slower than the per-row
+// one at combine-heavy size.
+#ifndef MOE_CS_COOP_UNITS
+#define MOE_CS_COOP_UNITS 16
+#endif
+constexpr int kCcThreads = 1024, kCcUnroll = MOE_CS_COOP_UNITS;
 __global__ __launch_bounds__(kCcThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                const int* __restrict__ row_src,
                                                                uint16_t* __restrict__ comb) {
@@ -572,7 +578,10 @@ __global__ __launch_bounds__(kCpThreads) void k_copy16(v4u* __restrict__ dst, co
 #ifndef MOE_CS_COOP
 #define MOE_CS_COOP 1
 #endif
-constexpr int64_t kCcMinRows = 131072;   // rows from which the cooperative form is used
+#ifndef MOE_CS_COOP_MIN_ROWS
+#define MOE_CS_COOP_MIN_ROWS 131072
+#endif
+constexpr int64_t kCcMinRows = MOE_CS_COOP_MIN_ROWS;   // rows from which the cooperative form is used
 
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,
                      hipStream_t st) {
