@@ -105,35 +105,84 @@ def _traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(T_sample: int):
-    """The oracle, as it stands, on a bounded sample of the same workload: the
-    same N, H, E, k with T_sample tokens per rank; single-threaded NumPy."""
+def _oracle_run(cfg, T_sample: int, ready=None):
+    """The oracle's four phases on seeded inputs of `cfg` with T_sample tokens
+    per rank; input generation is not timed.  Returns (algorithmic bytes,
+    seconds, start, end) with start/end on the monotonic clock.  `ready`, if
+    given, is waited on once the inputs exist (a barrier across processes)."""
     import numpy as np
     import torch
 
     import workloads as W
     from oracle import moe_oracle as O
 
-    cfg = W.CONFIGS["combine_heavy"]
     idx, w = W.routing(cfg, T_sample)
     x = W.tokens(cfg, "cpu", T_sample).float().numpy()
-    t0 = time.perf_counter()
+    if ready is not None:
+        ready.wait()
+    t0 = time.monotonic()
     lay = O.layout(idx, cfg.E, cfg.N)
     rq, rs = O.dispatch_send(x, lay)
     xq, xs, rsrc = O.dispatch_recv(rq, rs, lay)
-    t1 = time.perf_counter()
+    t1 = time.monotonic()
     y = W.expert_outputs(cfg, lay.total_rows, "cpu").view(torch.int16).numpy().view(np.uint16)
-    t2 = time.perf_counter()
+    t2 = time.monotonic()
     comb = O.combine_send(y, rsrc, cfg.N, T_sample, cfg.k)
     O.combine_recv(comb, lay.send_pos, w, T_sample, cfg.k)
-    t3 = time.perf_counter()
-    sec = (t1 - t0) + (t3 - t2)
+    t3 = time.monotonic()
     nb = algorithmic_bytes(cfg.N, T_sample, cfg.H, cfg.E, cfg.k)
-    nbytes = sum(nb[p] for p in PHASES)
+    return sum(nb[p] for p in PHASES), (t1 - t0) + (t3 - t2), t0, t3
+
+
+def note(msg: str) -> None:
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(T_sample: int):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    same N, H, E, k with T_sample tokens per rank; single-threaded NumPy."""
+    import workloads as W
+    cfg = W.CONFIGS["combine_heavy"]
+    nbytes, sec, _, _ = _oracle_run(cfg, T_sample)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(sec, 2),
             "sample": f"combine_heavy shape with T={T_sample} tokens/rank (N={cfg.N}, H={cfg.H}, E={cfg.E}, "
                       f"k={cfg.k}): all four phases, single-threaded NumPy, input generation excluded"}
+
+
+def _oracle_proc(seed, T_sample, ready, out):
+    import torch
+    torch.set_num_threads(1)   # one core per process, input generation included
+    import workloads as W
+    out.put(_oracle_run(W.CONFIGS["combine_heavy"].with_(seed=seed), T_sample, ready))
+
+
+def cpu_baseline_parallel(T_sample: int, procs: int):
+    """The same oracle in `procs` processes at once, each on its own seeded
+    sample of T_sample tokens per rank (independent problems, so the
+    processes share nothing); throughput = all their bytes over the span from
+    the first start to the last end.  Fresh interpreters ("spawn"), started
+    before this process touches the GPU."""
+    import multiprocessing as mp
+    import workloads as W
+    ctx = mp.get_context("spawn")
+    ready, out = ctx.Barrier(procs), ctx.Queue()
+    seed = W.CONFIGS["combine_heavy"].seed
+    ps = [ctx.Process(target=_oracle_proc, args=(seed + 1 + i, T_sample, ready, out)) for i in range(procs)]
+    for p in ps:
+        p.start()
+    res = [out.get() for _ in ps]
+    for p in ps:
+        p.join()
+    nbytes = sum(r[0] for r in res)
+    span = max(r[3] for r in res) - min(r[2] for r in res)
+    cfg = W.CONFIGS["combine_heavy"]
+    return {"value": round(nbytes / span / 1e9, 3), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "seconds": round(span, 2),
+            "sample": f"{procs} processes, each the combine_heavy shape with T={T_sample} tokens/rank "
+                      f"(N={cfg.N}, H={cfg.H}, E={cfg.E}, k={cfg.k}) on its own seed: all four phases, "
+                      f"NumPy, input generation excluded"}
 
 
 def main():
@@ -159,6 +208,16 @@ def main():
 
     cfg = W.CONFIGS[args.workload]
     T, Tc = cfg.T, cfg.Tc
+    # The CPU baselines run first: the parallel one starts processes, which
+    # should happen before this process initialises the GPU.
+    cpu_single = cpu_par = None
+    if not args.no_cpu_baseline:
+        note("cpu baseline: the oracle, one process")
+        cpu_single = cpu_baseline(args.cpu_sample_tokens)
+        procs = min(16, len(os.sched_getaffinity(0)))
+        note(f"cpu baseline: the oracle, {procs} processes")
+        cpu_par = cpu_baseline_parallel(max(1, args.cpu_sample_tokens // 8), procs)
+    note(f"gpu: {cfg.name}, {args.warmup} warm-up and {args.steps} timed steps")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -241,6 +300,7 @@ def main():
 
     graph_step_ms = graph_ms(moe.moe_dispatch_send)
 
+    note("single-launch dispatch")
     # The single-launch dispatch (moe_dispatch_send_ll, one routing chunk per
     # rank only) in the same step in place of moe_dispatch_send: its phase
     # time, the eager and graph-replayed step, and a bitwise comparison of its
@@ -309,6 +369,7 @@ def main():
                                 "same_send_pos": same_e}
         del Be, ye, comb_e, out_e
 
+    note("direct dispatch")
     # The direct dispatch (moe_dispatch_direct: rows stored straight at their
     # expert-major rows, no receive regions, no unpack) on the same inputs
     # and buffers, compared bit for bit with the two-call path's outputs.
@@ -332,6 +393,7 @@ def main():
     direct_ll = time_direct(moe.moe_dispatch_direct_ll) if T * cfg.k <= 4096 and T > 0 else None
     del ref
 
+    note("pulling and partial combines")
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(2):
@@ -400,6 +462,7 @@ def main():
     copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    note("fastest layer")
     # The fastest composition of one layer on one GPU: the faster dispatch --
     # the direct one, or the send (single launch with early rows where it
     # applies, else the multi-launch call) plus the unpack -- then the
@@ -529,10 +592,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(kernel, cfg.name)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu_single,
+        "cpu_baseline_parallel": cpu_par,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
 
 
