@@ -101,23 +101,24 @@ __device__ __forceinline__ void count_chunk(const Dims& D, const Ws& W, const in
   int* wr = run + w * D.E;
 #pragma unroll
   for (int bt = 0; bt < kMaxBatches; ++bt) {
-    if (bt * kWave >= per_wave) break;
-    const int e = ev[bt];   // still the plain expert id here
-    if (e >= 0) atomicOr(&wm[e], 1ull << lane);
-    __builtin_amdgcn_wave_barrier();
-    unsigned long long m = 0ull;
-    int r = -1;
-    if (e >= 0) {
-      m = wm[e];
-      r = wr[e] + __popcll(m & ((1ull << lane) - 1ull));
+    if (bt * kWave < per_wave) {   // wave-uniform
+      const int e = ev[bt];   // still the plain expert id here
+      if (e >= 0) atomicOr(&wm[e], 1ull << lane);
+      __builtin_amdgcn_wave_barrier();
+      unsigned long long m = 0ull;
+      int r = -1;
+      if (e >= 0) {
+        m = wm[e];
+        r = wr[e] + __popcll(m & ((1ull << lane) - 1ull));
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && (m >> lane) == 1ull) {   // highest lane of its expert group
+        wr[e] += __popcll(m);
+        wm[e] = 0ull;
+      }
+      __builtin_amdgcn_wave_barrier();
+      ev[bt] = e >= 0 ? (r << 11) | (e + 1) : 0;
     }
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0 && (m >> lane) == 1ull) {   // highest lane of its expert group
-      wr[e] += __popcll(m);
-      wm[e] = 0ull;
-    }
-    __builtin_amdgcn_wave_barrier();
-    ev[bt] = e >= 0 ? (r << 11) | (e + 1) : 0;
   }
   if (__any(bad) && lane == 0) atomicOr(W.err, MOE_FLAG_BADID);
   __syncthreads();
@@ -165,9 +166,8 @@ __device__ __forceinline__ void count_chunk(const Dims& D, const Ws& W, const in
   __syncthreads();
 #pragma unroll
   for (int bt = 0; bt < kMaxBatches; ++bt) {
-    if (bt * kWave >= per_wave) break;
     const int i = c0 + bt * kWave + lane;
-    if (i >= cend) continue;
+    if (bt * kWave >= per_wave || i >= cend) continue;
     const int e = (ev[bt] & 0x7FF) - 1;
     const int v = e >= 0 ? wr[e] + (ev[bt] >> 11) : -1;
     if (D.B == 1) {
