@@ -18,7 +18,10 @@ recv), when every rank's slots fit one routing chunk (T*k <= 4096) its single
 launch (moe_dispatch_direct_ll) and the step with the single-launch
 moe_dispatch_send_ll in place of moe_dispatch_send (also with early rows),
 and the fastest composition of one layer (the fastest of these dispatches,
-the pulling combine) as whole steps.
+the pulling combine) as whole steps, and cold-cache phase times (1 GiB of
+scratch written before each call).  The CPU baselines (the oracle in one
+process, and in min(16, cores) processes on independent problems) run first,
+before the GPU is touched.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
