@@ -21,7 +21,11 @@
 //   k_comb_send_partial  send-side partial sums: one bf16 row per (token,
 //                        destination rank) group ("Evaluation:
 //                        dispatch/combine latency": accumulating on the send
-//                        side cuts the data sent)
+//                        side cuts the data sent); one 1024-thread
+//                        workgroup per CU on chunks of tokens,
+//                        thread-interleaved 16-byte units
+//                        (k_comb_send_partial_tokens: one wave per token,
+//                        below 16384 tokens)
 //   k_comb_recv_partial  the receive side of it: fp32 sum of a token's group
 //                        rows, bf16 out
 //   k_copy16             plain streaming copy (measurement aid)
@@ -443,7 +447,8 @@ __global__ __launch_bounds__(kCoThreads) void k_comb_pull(Dims D, Ws W, const ui
   combine_tokens_coop<CombMode::kPull>(D, W, y, idx, send_pos, topk_w, out);
 }
 
-// Send-side partial sums, token by token (one wave per token): for each
+// Send-side partial sums, token by token (one wave per token; the form for
+// problems below 16384 tokens): for each
 // group (a token's slots whose rows sit on one rank) in leader order, its
 // members in slot order, acc = fl(acc + fl(w * y)) with no fused
 // multiply-add, rounded to bf16 and stored where the leader's row returns
@@ -457,7 +462,7 @@ constexpr int kSpWaves = kSendPartialShape.waves, kSpThreads = kSendPartialShape
 #define MOE_SEND_PIECES 2
 #endif
 constexpr int kSendPieces = MOE_SEND_PIECES;
-__global__ __launch_bounds__(kSpThreads) void k_comb_send_partial(Dims D, Ws W, const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kSpThreads) void k_comb_send_partial_tokens(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                    const int* __restrict__ idx,
                                                                    const int* __restrict__ send_pos,
                                                                    const float* __restrict__ topk_w,
@@ -578,6 +583,121 @@ __global__ __launch_bounds__(kCpThreads) void k_copy16(v4u* __restrict__ dst, co
 #ifndef MOE_CS_COOP
 #define MOE_CS_COOP 1
 #endif
+// The send-side partial sums with the whole workgroup on a chunk of
+// consecutive tokens (the plain copy's pattern, as k_comb_send): each slot's
+// expert-major row, weight, destination rank and, for a group leader, its
+// comb position are resolved into LDS; then thread t forms the 16-byte
+// units t, t + kPsThreads, ... of every group row of the chunk's tokens,
+// each from the same 16 bytes of the group's member rows, summed in slot
+// order exactly as k_comb_send_partial does.
+#ifndef MOE_SP_COOP_PAIR
+#define MOE_SP_COOP_PAIR 1
+#endif
+#ifndef MOE_SP_COOP_UNITS
+#define MOE_SP_COOP_UNITS 8
+#endif
+constexpr int kPsThreads = 1024, kPsUnits = MOE_SP_COOP_UNITS, kPsTable = 2048, kPsPair = MOE_SP_COOP_PAIR;
+__global__ __launch_bounds__(kPsThreads) void k_comb_send_partial(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                                       const int* __restrict__ idx,
+                                                                       const int* __restrict__ send_pos,
+                                                                       const float* __restrict__ topk_w,
+                                                                       uint16_t* __restrict__ comb) {
+  __shared__ int t_row[kPsTable], t_dest[kPsTable], t_out[kPsTable];
+  __shared__ float t_w[kPsTable];
+  const int n16 = D.H / 8, k = D.k;
+  int ntok = kPsThreads * kPsUnits / n16;                 // tokens per chunk
+  ntok = max(1, min(ntok, kPsTable / k));
+  const v4u* __restrict__ ys = reinterpret_cast<const v4u*>(y);
+  v4u* __restrict__ cs = reinterpret_cast<v4u*>(comb);
+  int lo, hi;
+  block_range(D.N * D.T, lo, hi);
+  for (int t0 = lo; t0 < hi; t0 += ntok) {
+    const int nt = min(ntok, hi - t0);
+    for (int i = threadIdx.x; i < nt * k; i += kPsThreads) {
+      const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
+      const int s = (t0 + i / k) / D.T;
+      const int sp = send_pos[slot];
+      const int e = idx[slot];
+      const int row = em_row_of(D, W, s, e, sp);
+      t_row[i] = row;
+      t_w[i] = topk_w[slot];
+      t_dest[i] = row >= 0 ? e / D.L : -1;
+      t_out[i] = row >= 0 ? s * D.TK + sp : -1;
+    }
+    __syncthreads();
+    // A slot with a row leads its group unless an earlier slot of the token
+    // has a row on the same rank.
+    for (int i = threadIdx.x; i < nt * k; i += kPsThreads) {
+      const int j = i % k, b = i - j, d = t_dest[i];
+      bool lead = d >= 0;
+      for (int jj = 0; jj < j; ++jj) lead = lead && t_dest[b + jj] != d;
+      if (!lead) t_out[i] = -1;
+    }
+    __syncthreads();
+    const int nf = nt * n16;
+    if (k <= kSlotGroup) {
+      // kPsPair units per thread and step, all their slot loads issued first.
+      for (int f0 = threadIdx.x; f0 < nf; f0 += kPsThreads * kPsPair) {
+        v4u v[kPsPair][kSlotGroup];
+#pragma unroll
+        for (int q = 0; q < kPsPair; ++q) {
+          const int f = f0 + q * kPsThreads, tt = f / n16, c = f - tt * n16, b = tt * k;
+#pragma unroll
+          for (int j = 0; j < kSlotGroup; ++j) {
+            const int r = f < nf && j < k ? t_row[b + j] : -1;
+            v[q][j] = r >= 0 ? ld16(ys + (int64_t)r * n16 + c) : v4u{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kPsPair; ++q) {
+          const int f = f0 + q * kPsThreads, tt = f / n16, c = f - tt * n16, b = tt * k;
+          if (f >= nf) continue;
+#pragma unroll
+          for (int g = 0; g < kSlotGroup; ++g) {
+            const int og = g < k ? t_out[b + g] : -1;
+            if (og < 0) continue;   // not a leader
+            const int dg = t_dest[b + g];
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int j = g; j < kSlotGroup; ++j)
+              if (j < k && t_dest[b + j] == dg) acc_row8(acc, t_w[b + j], v[q][j]);
+            st16(cs + (int64_t)og * n16 + c, pack_bf16x8(acc));
+          }
+        }
+      }
+    } else {
+      for (int f = threadIdx.x; f < nf; f += kPsThreads) {
+        const int tt = f / n16, c = f - tt * n16, b = tt * k;
+        for (int g = 0; g < k; ++g) {
+          const int og = t_out[b + g];
+          if (og < 0) continue;
+          const int dg = t_dest[b + g];
+          float acc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+          for (int j0 = g; j0 < k; j0 += kSlotGroup) {
+            v4u v[kSlotGroup];
+            int rr[kSlotGroup];
+#pragma unroll
+            for (int jj = 0; jj < kSlotGroup; ++jj) {
+              const int j = j0 + jj;
+              rr[jj] = j < k && t_dest[b + j] == dg ? t_row[b + j] : -1;
+              v[jj] = rr[jj] >= 0 ? ld16(ys + (int64_t)rr[jj] * n16 + c) : v4u{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSlotGroup; ++jj)
+              if (rr[jj] >= 0) acc_row8(acc, t_w[b + j0 + jj], v[jj]);
+          }
+          st16(cs + (int64_t)og * n16 + c, pack_bf16x8(acc));
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 #ifndef MOE_CS_COOP_MIN_ROWS
 #define MOE_CS_COOP_MIN_ROWS 131072
 #endif
@@ -628,12 +748,26 @@ int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* i
   return launch("k_comb_pull_tokens", k_comb_pull_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
+#ifndef MOE_SP_COOP
+#define MOE_SP_COOP 1
+#endif
+#ifndef MOE_SP_COOP_MIN_TOKENS
+#define MOE_SP_COOP_MIN_TOKENS 16384
+#endif
+constexpr int64_t kPsMinTokens = MOE_SP_COOP_MIN_TOKENS;   // tokens (N*T) from which the cooperative form is used
+
 int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                              const float* w, uint16_t* comb, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
+  if (MOE_SP_COOP && (int64_t)D.N * D.T >= kPsMinTokens) {
+    const int64_t need = ((int64_t)D.N * D.T * (D.H / 8) + kPsThreads * kPsUnits - 1) / (kPsThreads * kPsUnits);
+    const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
+    return launch("k_comb_send_partial", k_comb_send_partial, dim3(grid), dim3(kPsThreads), 0, st, D, W, y,
+                  idx, send_pos, w, comb);
+  }
   const int grid = stream_grid(kSendPartialShape, cus, (int64_t)D.N * D.T, kSpWaves);
-  return launch("k_comb_send_partial", k_comb_send_partial, dim3(grid), dim3(kSpThreads), 0, st, D, W, y, idx,
-                send_pos, w, comb);
+  return launch("k_comb_send_partial_tokens", k_comb_send_partial_tokens, dim3(grid), dim3(kSpThreads), 0, st, D, W,
+                y, idx, send_pos, w, comb);
 }
 
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,

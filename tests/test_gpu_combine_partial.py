@@ -64,6 +64,23 @@ def test_shapes(N, T, H, E, k):
     _full_check(run_all(_cfg(f"cp{N}_{T}_{H}_{E}_{k}", N=N, T=T, H=H, E=E, k=k), T))
 
 
+@pytest.mark.parametrize("N,T,H,E,k,tight", [
+    (8, 2100, 256, 64, 8, False),    # k <= 8: every group formed from registers
+    (4, 4100, 384, 64, 12, False),   # k > 8, ragged token chunks (170 tokens per chunk)
+    (8, 2100, 256, 64, 8, True),     # fixed regions that overflow: dropped slots join no group
+])
+def test_many_tokens(N, T, H, E, k, tight):
+    """At least 16384 tokens (N*T): the size from which the send half takes
+    its large-problem form; every element checked."""
+    cfg = _cfg(f"cp_many{N}_{k}_{tight}", N=N, T=T, H=H, E=E, k=k)
+    idx, w = W.routing(cfg, T)
+    R = int(O.layout(idx, E, N).recv_total.max()) - 40 if tight else 0
+    r = run_all(cfg, T, R, idx=idx, w=w)
+    assert N * T >= 16384
+    assert bool(r["flags"] & O.FLAG_OVERFLOW) == tight
+    _full_check(r, R)
+
+
 def test_all_slots_on_one_rank_equals_plain_combine():
     cfg = _cfg("cp_forced", N=8, T=200, H=256, E=64, k=8, forced_rank0=True)
     r = run_all(cfg, 200)
