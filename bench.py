@@ -19,9 +19,12 @@ launch (moe_dispatch_direct_ll) and the step with the single-launch
 moe_dispatch_send_ll in place of moe_dispatch_send (also with early rows),
 and the fastest composition of one layer (the fastest of these dispatches,
 the pulling combine) as whole steps, and cold-cache phase times (1 GiB of
-scratch written before each call).  The CPU baselines (the oracle in one
-process, and in min(16, cores) processes on independent problems) run first,
-before the GPU is touched.
+scratch written before each call).  Each phase's rate is also given as a
+fraction of its access pattern's ceiling on the same GPU: a plain stream of
+the same shape (moe_stream fan-out for the pack, moe_copy for unpack and
+combine send, moe_stream reduction for the receive-side sum).  The CPU
+baselines (the oracle in one process, and in min(16, cores) processes on
+independent problems) run first, before the GPU is touched.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -465,6 +468,37 @@ def main():
     copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    note("pattern ceilings")
+    # The achievable rate of each phase's access pattern on this GPU: a plain
+    # stream (moe_stream, moe_copy) over the phase's row bytes, free of its
+    # row lookups and arithmetic.  The pack reads a bf16 row and stores k fp8
+    # rows (fan-out); unpack and combine send are copies; the receive-side
+    # sum reads k bf16 rows and stores one (reduction).
+    def stream_gbs(pattern, units, src_units, dst_units, moved_units):
+        s_ = torch.empty(src_units * 16, dtype=torch.uint8, device=dev)
+        d_ = torch.empty(dst_units * 16, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            moe.moe_stream(pattern, cfg.k, d_, s_, units)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            moe.moe_stream(pattern, cfg.k, d_, s_, units)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del s_, d_
+        return moved_units * 16 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    u_fan = cfg.N * T * cfg.H // 16            # one fp8 copy of every dispatched token, in 16-B units
+    u_red = cfg.N * Tc * cfg.H * 2 // 16       # the bf16 combine output, in 16-B units
+    fan_gbs = stream_gbs(moe.STREAM_FANOUT, u_fan, 2 * u_fan, cfg.k * u_fan, (2 + cfg.k) * u_fan)
+    red_gbs = stream_gbs(moe.STREAM_REDUCE, u_red, cfg.k * u_red, u_red, (cfg.k + 1) * u_red)
+    ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays",
+                                  "GB/s": round(fan_gbs, 1)},
+                "dispatch_recv": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
+                "combine_send": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
+                "combine_recv": {"pattern": f"reduction: {cfg.k} arrays read, one stored",
+                                 "GB/s": round(red_gbs, 1)}}
+
     note("fastest layer")
     # The fastest composition of one layer on one GPU: the faster dispatch --
     # the direct one, or the send (single launch with early rows where it
@@ -544,6 +578,8 @@ def main():
 
     med_ms = np.median(ms, axis=0)
     phase_info = {name: info(name, per_phase_ms[p], p90_ms[p], med_ms[p]) for p, name in enumerate(PHASES)}
+    for name, d in phase_info.items():
+        d["of_pattern_ceiling"] = round(d["GB/s"] / ceilings[name]["GB/s"], 4)
     if single is not None:
         single["dispatch_send"] = info("dispatch_send", single_ms, single_p90)
         single["early_rows"]["dispatch_send"] = info("dispatch_send", early_ms)
@@ -592,6 +628,7 @@ def main():
         "single_launch_dispatch": single,
         "fastest_layer": fast,
         "copy_ceiling_GB/s": round(copy_gbs, 1),
+        "pattern_ceilings": ceilings,
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(kernel, cfg.name)},

@@ -319,6 +319,8 @@ int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, cons
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
                              uint16_t* out, int cus, hipStream_t st);
 int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
+constexpr int kStreamFanout = 1, kStreamReduce = 2;   // moe_stream patterns (MOE_STREAM_*)
+int launch_stream(int pattern, int k, void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 
 }  // namespace moe
