@@ -20,9 +20,9 @@ moe_dispatch_send_ll in place of moe_dispatch_send (also with early rows),
 and the fastest composition of one layer (the fastest of these dispatches,
 the pulling combine) as whole steps, and cold-cache phase times (1 GiB of
 scratch written before each call).  Each phase's rate is also given as a
-fraction of its access pattern's ceiling on the same GPU: a plain stream of
-the same shape (moe_stream fan-out for the pack, moe_copy for unpack and
-combine send, moe_stream reduction for the receive-side sum).  The CPU
+fraction of its access pattern's ceiling: a plain stream of the same shape
+on the phase's own buffers (moe_stream fan-out for the pack, moe_copy for
+unpack and combine send, moe_stream reduction for the receive-side sum).  The CPU
 baselines (the oracle in one process, and in min(16, cores) processes on
 independent problems) run first, before the GPU is touched.
 
@@ -452,53 +452,6 @@ def main():
             cold[i, p] = e0.elapsed_time(e1)
     del scratch
 
-    # Achievable read+write rate: a plain copy of the dominant phase's bytes.
-    dom = max(range(4), key=lambda p: per_phase_ms[p])
-    copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
-    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        moe.moe_copy(dst, src, copy_bytes)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        moe.moe_copy(dst, src, copy_bytes)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
-    note("pattern ceilings")
-    # The achievable rate of each phase's access pattern on this GPU: a plain
-    # stream (moe_stream, moe_copy) over the phase's row bytes, free of its
-    # row lookups and arithmetic.  The pack reads a bf16 row and stores k fp8
-    # rows (fan-out); unpack and combine send are copies; the receive-side
-    # sum reads k bf16 rows and stores one (reduction).
-    def stream_gbs(pattern, units, src_units, dst_units, moved_units):
-        s_ = torch.empty(src_units * 16, dtype=torch.uint8, device=dev)
-        d_ = torch.empty(dst_units * 16, dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            moe.moe_stream(pattern, cfg.k, d_, s_, units)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            moe.moe_stream(pattern, cfg.k, d_, s_, units)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        del s_, d_
-        return moved_units * 16 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-
-    u_fan = cfg.N * T * cfg.H // 16            # one fp8 copy of every dispatched token, in 16-B units
-    u_red = cfg.N * Tc * cfg.H * 2 // 16       # the bf16 combine output, in 16-B units
-    fan_gbs = stream_gbs(moe.STREAM_FANOUT, u_fan, 2 * u_fan, cfg.k * u_fan, (2 + cfg.k) * u_fan)
-    red_gbs = stream_gbs(moe.STREAM_REDUCE, u_red, cfg.k * u_red, u_red, (cfg.k + 1) * u_red)
-    ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays",
-                                  "GB/s": round(fan_gbs, 1)},
-                "dispatch_recv": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
-                "combine_send": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
-                "combine_recv": {"pattern": f"reduction: {cfg.k} arrays read, one stored",
-                                 "GB/s": round(red_gbs, 1)}}
-
     note("fastest layer")
     # The fastest composition of one layer on one GPU: the faster dispatch --
     # the direct one, or the send (single launch with early rows where it
@@ -563,6 +516,45 @@ def main():
     flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
         raise SystemExit(f"device error flags {flags:#x} in the timed steps")
+
+    # Achievable rates of the phases' access patterns, on the phases' own
+    # buffers (where a buffer lands in memory moves a stream's rate by up to
+    # ~10%): plain streams free of the row lookups and arithmetic.  The pack
+    # reads a bf16 token row and stores k fp8 rows (moe_stream fan-out, tokens
+    # -> recv_q); unpack and combine send are copies (moe_copy, y -> comb, the
+    # dominant phase's bytes); the receive-side sum reads k bf16 rows and
+    # stores one (moe_stream reduction, comb -> out).  They overwrite recv_q,
+    # comb and out, so they run after everything else.
+    note("pattern ceilings")
+    dom = max(range(4), key=lambda p: per_phase_ms[p])
+    copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
+    assert copy_bytes <= y.numel() * 2 and copy_bytes <= Bc.comb.numel() * 2
+
+    def rate(fn, moved):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return moved * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    u_fan = cfg.N * T * cfg.H // 16            # one fp8 copy of every dispatched token, in 16-B units
+    u_red = cfg.N * Tc * cfg.H * 2 // 16       # the bf16 combine output, in 16-B units
+    assert 2 * u_fan * 16 == x.numel() * 2 and cfg.k * u_fan * 16 <= B.recv_q.numel()
+    assert cfg.k * u_red * 16 == Bc.comb.numel() * 2 and u_red * 16 == Bc.out.numel() * 2
+    copy_gbs = rate(lambda: moe.moe_copy(Bc.comb, y, copy_bytes), 2 * copy_bytes)
+    fan_gbs = rate(lambda: moe.moe_stream(moe.STREAM_FANOUT, cfg.k, B.recv_q, x, u_fan), (2 + cfg.k) * u_fan * 16)
+    red_gbs = rate(lambda: moe.moe_stream(moe.STREAM_REDUCE, cfg.k, Bc.out, Bc.comb, u_red),
+                   (cfg.k + 1) * u_red * 16)
+    ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays",
+                                  "GB/s": round(fan_gbs, 1)},
+                "dispatch_recv": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
+                "combine_send": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
+                "combine_recv": {"pattern": f"reduction: {cfg.k} arrays read, one stored",
+                                 "GB/s": round(red_gbs, 1)}}
 
     def info(name, t_ms, t90=None, t50=None):
         """Mean time t_ms (the roofline uses the mean launch duration), with
