@@ -1,0 +1,62 @@
+"""bench.py's host-side arithmetic, without a GPU: the per-phase byte counts
+behind every GB/s figure (each phase's inputs read once and outputs written
+once, counted here from the arrays the calls take), the (token, destination
+rank) group count of the send-side partial combine (brute force), and the
+one-GPU guard of --gpus."""
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+
+
+@pytest.mark.parametrize("N,T,H,E,k,Tc", [(16, 4096, 7168, 256, 8, None), (64, 128, 7168, 384, 8, 4096),
+                                          (16, 128, 2048, 128, 8, None), (4, 7, 256, 8, 3, 5)])
+def test_phase_bytes_are_the_arrays_each_call_touches(N, T, H, E, k, Tc):
+    Tcc = T if Tc is None else Tc
+    P, Pc = N * T * k, N * Tcc * k
+    tokens, fp8_row, scale_row, bf16_row = N * T * H * 2, H, 4 * (H // 128), 2 * H
+    ids, pos, w = 4 * N * T * k, 4 * N * T * k, 4 * N * Tcc * k
+    counts = 4 * N * E
+    G = Pc - N * Tcc   # any group count in [N*Tc, Pc]
+    nb = bench.algorithmic_bytes(N, T, H, E, k, Tc, G)
+    # dispatch send: tokens and ids in; every slot's fp8 row + scales, send_pos and the count table out
+    assert nb["dispatch_send"] == tokens + ids + P * (fp8_row + scale_row) + pos + counts
+    # direct dispatch: the same plus one row_src entry per row
+    assert nb["dispatch_direct"] == nb["dispatch_send"] + 4 * P
+    # dispatch recv: every received row read once and written once
+    assert nb["dispatch_recv"] == 2 * P * (fp8_row + scale_row)
+    # combine send: every expert output row read once, written once
+    assert nb["combine_send"] == 2 * Pc * bf16_row
+    # combine recv: k rows, k weights and k positions per token in, one bf16 row out
+    out = N * Tcc * H * 2
+    assert nb["combine_recv"] == Pc * bf16_row + out + w + 4 * N * Tcc * k
+    # pull: the same rows read in place, plus the ids that locate them
+    assert nb["combine_pull"] == nb["combine_recv"] + 4 * N * Tcc * k
+    # partial: send reads every row and writes one row per group; recv reads the groups
+    assert nb["combine_send_partial"] == Pc * bf16_row + G * bf16_row + 3 * 4 * N * Tcc * k
+    assert nb["combine_recv_partial"] == G * bf16_row + out + 2 * 4 * N * Tcc * k
+
+
+def test_combine_heavy_phase_bytes():
+    nb = bench.algorithmic_bytes(16, 4096, 7168, 256, 8)
+    assert [round(nb[p] / 1e9, 3) for p in bench.PHASES] == [4.819, 7.751, 15.032, 8.46]
+
+
+def test_group_count_matches_brute_force():
+    rng = np.random.default_rng(5)
+    for N, T, E, k in [(4, 9, 16, 3), (8, 5, 64, 8), (2, 11, 4, 4), (1, 3, 8, 2)]:
+        L = E // N
+        idx = np.stack([np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]) for _ in range(N)])
+        want = sum(len({int(e) // L for e in idx[s, t]}) for s in range(N) for t in range(T))
+        assert bench.combine_groups(idx.astype(np.int32), L) == want
+        assert N * T <= want <= N * T * k
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       cwd=bench.ROOT, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
