@@ -620,7 +620,7 @@ __global__ __launch_bounds__(kCpThreads) void k_stream_fanout(v4u* __restrict__ 
   }
 }
 
-constexpr int stream_reduce_units(int K) { return K <= 3 ? 8 : (K == 4 ? 6 : 32 / K); }   // without spills
+constexpr int stream_reduce_units(int K) { return K <= 3 ? 8 : (K == 4 ? 6 : 32 / K); }   // units per thread
 
 template <int K>
 __global__ __launch_bounds__(kCpThreads) void k_stream_reduce(v4u* __restrict__ dst, const v4u* __restrict__ src,

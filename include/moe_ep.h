@@ -343,7 +343,7 @@ int moe_copy(void *dst, const void *src, int64_t nbytes, void *stream);
  *     stores 16 bytes at dst unit i: the receive-side sum's k rows in, one
  *     out.  src holds k*n16 units, dst n16.
  * Errors: MOE_EINVAL for another pattern, k outside [1, 8] or n16 < 0;
- * MOE_ERANGE if the byte counts overflow; MOE_ENULL / MOE_EALIGN.
+ * MOE_ERANGE for n16 above 2^40 (16 TiB); MOE_ENULL / MOE_EALIGN.
  */
 #define MOE_STREAM_FANOUT 1
 #define MOE_STREAM_REDUCE 2

@@ -117,7 +117,7 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     assert lib.moe_stream(1, 0, _p(A), _p(A), 16, None) == -1          # k outside [1, 8]
     assert lib.moe_stream(2, 9, _p(A), _p(A), 16, None) == -1
     assert lib.moe_stream(2, 8, _p(A), _p(A), -1, None) == -1          # negative count
-    assert lib.moe_stream(2, 8, _p(A), _p(A), 1 << 62, None) == -4     # bytes overflow
+    assert lib.moe_stream(2, 8, _p(A), _p(A), (1 << 40) + 1, None) == -4   # above 2^40 units
     assert lib.moe_stream(1, 8, None, _p(A), 16, None) == -2
     assert lib.moe_stream(1, 8, _p(A), _p(A + 8), 16, None) == -3
     assert lib.moe_layout_export(s, None, None, None, None, None, None, None) == -2
