@@ -606,9 +606,11 @@ def main():
                                ((per_phase_ms[0] + per_phase_ms[1]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "combine_frac": round((nbytes["combine_send"] + nbytes["combine_recv"]) /
                               ((per_phase_ms[2] + per_phase_ms[3]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same),
+        "combine_pull": dict(info("combine_pull", pull_ms), same_bytes_as_send_recv=pull_same,
+                             of_pattern_ceiling=round(nbytes["combine_pull"] / (pull_ms * 1e-3) / 1e9 / red_gbs, 4)),
         "dispatch_direct": dict(info("dispatch_direct", direct_ms, direct_p90, direct_med),
                                 same_bytes_as_send_recv=bool(direct_same),
+                                of_pattern_ceiling=round(nbytes["dispatch_direct"] / (direct_ms * 1e-3) / 1e9 / fan_gbs, 4),
                                 single_launch=None if direct_ll is None else dict(
                                     info("dispatch_direct", *direct_ll[:3]), same_bytes_as_send_recv=direct_ll[3])),
         "combine_partial": {"groups_per_token": round(G / (cfg.N * Tc), 3),
