@@ -118,6 +118,21 @@ def test_shapes(N, T, H, E, k):
     _full_case(cfg, T)
 
 
+@pytest.mark.parametrize("N,T,H,E,k,C", [
+    (4, 4100, 1152, 32, 8, 0),   # 72 pieces per row, 56 tokens per chunk, ragged chunks
+    (8, 2048, 384, 64, 6, 96),   # fixed regions with early rows
+])
+def test_large_token_counts(N, T, H, E, k, C):
+    """Above 16384 tokens (where the combine kernels switch to their
+    cooperative forms), every element checked, packed and with early rows."""
+    cfg = _small(f"coop{N}_{T}_{H}", N=N, T=T, H=H, E=E, k=k)
+    if C == 0:
+        _full_case(cfg, T)
+    else:
+        idx, w = W.routing(cfg, T)
+        _full_case(cfg, T, _early_region(idx, cfg.E, cfg.N, C, 17), idx, w, early_rows=C)
+
+
 def test_skewed_small():
     cfg = _small("skew", N=8, T=600, H=256, E=48, k=8, skew=True)
     _full_case(cfg, 600)
