@@ -1,0 +1,25 @@
+"""The C ABI is usable from plain C: include/moe_ep.h compiles as C99 with
+warnings as errors, and a C program linked to libmoe_ep.so gets the sizes
+and host-side rejections the header documents (no GPU needed)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import combine_lds_atomic_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+def test_c_program_against_the_header(tmp_path):
+    exe = tmp_path / "c_abi_check"
+    libdir = os.path.dirname(moe.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), f"-L{libdir}", "-lmoe_ep",
+           f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
