@@ -438,6 +438,41 @@ def test_combine_single_slot_unit_weight_is_exact():
     assert (out.reshape(N * T, H) == comb[(np.arange(N)[:, None] * T + lay.send_pos[:, :, 0]).reshape(-1)]).all()
 
 
+def test_combine_sums_in_slot_order():
+    """The combine's float32 sum runs over slots 0..k-1 in that order.  Rows of
+    2^24, 1 and -2^24 with unit weights (tests/golden/combine_slot_order.json,
+    worked by hand) give sums that depend on the order of the additions: slot
+    order gives the fixture's values, while the reversed order and the order
+    of ascending expert id (the rows' order in the combine buffer) give others
+    on some token."""
+    g = _load("combine_slot_order.json")
+    idx = np.array(g["idx"])
+    N, T, k = idx.shape
+    H, E = g["H"], g["E"]
+    vals = np.array(g["y_slot_values"], np.float32)
+    w = np.array(g["w"], np.float32)
+    lay = O.layout(idx, E, N)
+    y = np.zeros((lay.total_rows, H), np.uint16)
+    for s in range(N):
+        for t in range(T):
+            for j in range(k):
+                y[lay.em_row[s, t, j]] = O.bf16_bits(np.full(H, vals[s, t, j], np.float32))
+    comb = O.combine_send(y, O.row_src(lay), N, T, k)
+    out = O.bf16_from_bits(O.combine_recv(comb, lay.send_pos, w, T, k)).astype(np.float64)
+    assert (out == np.array(g["out_slot_order"])[:, :, None]).all()
+    for s in range(N):
+        for t in range(T):
+            rows = np.stack([y[lay.em_row[s, t, j]] for j in range(k)])
+            assert (O.bf16_from_bits(O.combine_rows(rows, w[s, t])) == g["out_slot_order"][s][t]).all()
+            # The fixture tells the orders apart: the same rows summed
+            # reversed, or by expert id, give the fixture's other columns.
+            rev = O.bf16_from_bits(O.combine_rows(rows[::-1], w[s, t]))
+            by_e = O.bf16_from_bits(O.combine_rows(rows[np.argsort(idx[s, t])], w[s, t]))
+            assert (rev == g["out_reversed_order"][s][t]).all()
+            assert (by_e == g["out_expert_order"][s][t]).all()
+    assert g["out_reversed_order"] != g["out_slot_order"] and g["out_expert_order"] != g["out_slot_order"]
+
+
 def test_combine_skips_dropped_slots():
     rng = np.random.default_rng(16)
     N, T, H, E, k = 2, 4, 128, 4, 2
