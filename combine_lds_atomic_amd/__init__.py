@@ -82,8 +82,6 @@ _SIG = {
     "moe_combine_recv_partial": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "moe_layout_export": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
-    "moe_stream": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int64, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(lib, _name)
@@ -197,17 +195,6 @@ def moe_status(ws, stream=None) -> int:
 def moe_layout_export(sh, ws, cnt=None, send_off=None, recv_off=None, recv_total=None, base=None, stream=None):
     _check("moe_layout_export", lib.moe_layout_export(ctypes.byref(sh), _ptr(ws), _ptr(cnt), _ptr(send_off),
                                                       _ptr(recv_off), _ptr(recv_total), _ptr(base), _stream(stream)))
-
-
-def moe_copy(dst, src, nbytes: int, stream=None):
-    _check("moe_copy", lib.moe_copy(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)))
-
-
-STREAM_FANOUT, STREAM_REDUCE = 1, 2
-
-
-def moe_stream(pattern: int, k: int, dst, src, n16: int, stream=None):
-    _check("moe_stream", lib.moe_stream(int(pattern), int(k), _ptr(dst), _ptr(src), int(n16), _stream(stream)))
 
 
 from .buffers import Buffers, allocate  # noqa: E402  (device-memory plumbing)

@@ -1,7 +1,9 @@
-"""Build libmoe_ep.so (HIP, gfx950) in-tree with hipcc.
+"""Build libmoe_ep.so and libmoe_streams.so (HIP, gfx950) in-tree with hipcc.
 
 Each .hip source is compiled to an object in parallel, then linked into
-``combine_lds_atomic_amd/libmoe_ep.so``.  Usage: ``python
+``combine_lds_atomic_amd/libmoe_ep.so`` (dispatch / combine, include/moe_ep.h)
+and ``combine_lds_atomic_amd/libmoe_streams.so`` (the benchmark's plain
+streams, include/moe_streams.h).  Usage: ``python
 combine_lds_atomic_amd/build.py`` (or ``__graft_entry__.build()``); run it by
 path, since importing the package needs a library that exports every
 declared symbol.
@@ -19,7 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ep.so")
+STREAMS_LIB = os.path.join(PKG, "libmoe_streams.so")
 SOURCES = ["abi.hip", "layout.hip", "dispatch.hip", "combine.hip"]
+STREAMS_SOURCES = ["streams.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
@@ -38,8 +42,16 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, out: str = LIB, extra_flags: list[str] | None = None) -> str:
+    """Build libmoe_ep.so at `out` and, beside the default one, libmoe_streams.so."""
+    lib = _build_lib(SOURCES, out, "obj", verbose, extra_flags)
+    if out == LIB:
+        _build_lib(STREAMS_SOURCES, STREAMS_LIB, "obj_streams", verbose, extra_flags)
+    return lib
+
+
+def _build_lib(sources: list[str], out: str, objsub: str, verbose: bool, extra_flags: list[str] | None) -> str:
     cc = hipcc()
-    objdir = os.path.join(ROOT, "_build", "obj")
+    objdir = os.path.join(ROOT, "_build", objsub)
     os.makedirs(objdir, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
 
@@ -53,8 +65,8 @@ def build(verbose: bool = False, out: str = LIB, extra_flags: list[str] | None =
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        objs = list(ex.map(compile_one, sources))
     tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

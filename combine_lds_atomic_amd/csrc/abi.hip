@@ -376,21 +376,4 @@ int moe_layout_export(const moe_shape* shape, const void* ws, int32_t* cnt, int3
   return MOE_OK;
 }
 
-int moe_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
-  if (!dst || !src) return MOE_ENULL;
-  if (nbytes < 0 || nbytes % 16) return MOE_EINVAL;
-  if (!aligned(dst, 16) || !aligned(src, 16)) return MOE_EALIGN;
-  return launch_copy(dst, src, nbytes / 16, device_cus(), as_stream(stream));
-}
-
-int moe_stream(int pattern, int k, void* dst, const void* src, int64_t n16, void* stream) {
-  static_assert(MOE_STREAM_FANOUT == kStreamFanout && MOE_STREAM_REDUCE == kStreamReduce, "pattern codes");
-  if (pattern != MOE_STREAM_FANOUT && pattern != MOE_STREAM_REDUCE) return MOE_EINVAL;
-  if (k < 1 || k > 8 || n16 < 0) return MOE_EINVAL;
-  if (n16 > ((int64_t)1 << 40)) return MOE_ERANGE;   // keeps n16 * blockIdx within int64 in the kernels
-  if (!dst || !src) return MOE_ENULL;
-  if (!aligned(dst, 16) || !aligned(src, 16)) return MOE_EALIGN;
-  return launch_stream(pattern, k, dst, src, n16, device_cus(), as_stream(stream));
-}
-
 }  // extern "C"

@@ -28,7 +28,6 @@
 //                        below 16384 tokens)
 //   k_comb_recv_partial  the receive side of it: fp32 sum of a token's group
 //                        rows, bf16 out
-//   k_copy16             plain streaming copy (measurement aid)
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,12 +37,8 @@ constexpr int kCsWaves = kCombSendShape.waves, kCsThreads = kCombSendShape.threa
 // 16-B loads per lane issued together while copying a row.  A 7168-wide bf16
 // row needs 14; 32 (with 8-wave workgroups, two per CU) measured 2-5% faster
 // than 16 with 16-wave workgroups, in one process at three workloads.
-#ifndef MOE_CS_UNROLL
-#define MOE_CS_UNROLL 32
-#endif
-constexpr int kCsUnroll = MOE_CS_UNROLL;
+constexpr int kCsUnroll = 32;
 constexpr int kCrWaves = kCombRecvShape.waves, kCrThreads = kCombRecvShape.threads();
-constexpr int kCpThreads = kCopyShape.threads();
 
 // acc = fl(acc + fl(w * y)) in slot order, never fused into an FMA.
 __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
@@ -58,10 +53,7 @@ __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
 }
 
 constexpr int kSlotGroup = 8;
-#ifndef MOE_COMB_PIECES
-#define MOE_COMB_PIECES 2
-#endif
-constexpr int kCombPieces = MOE_COMB_PIECES;   // 1 KB pieces read per slot row per step
+constexpr int kCombPieces = 2;   // 1 KB pieces read per slot row per step
 
 // Expert-major row of a slot of source s with expert e and sender position
 // sp, found from the routing tables: the row combine_send would copy back.
@@ -166,10 +158,7 @@ __global__ __launch_bounds__(kCsThreads) void k_comb_send_rows(Dims D, Ws W, con
 // Each unit's load waits for its row_src: issuing the loads first, with
 // the row_src reads beside them, made this form 5% slower than the per-row
 // one at combine-heavy size.
-#ifndef MOE_CS_COOP_UNITS
-#define MOE_CS_COOP_UNITS 16
-#endif
-constexpr int kCcThreads = 1024, kCcUnroll = MOE_CS_COOP_UNITS;
+constexpr int kCcThreads = 1024, kCcUnroll = 16;
 __global__ __launch_bounds__(kCcThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                const int* __restrict__ row_src,
                                                                uint16_t* __restrict__ comb) {
@@ -377,10 +366,7 @@ __device__ __forceinline__ v4u pack_bf16x8(const float* acc) {
 // shape, 50% slower at the tiny one; hence the switch by token count.
 // One or two workgroups per CU and 4, 8 or 16 units per thread were within
 // 1% of each other.
-#ifndef MOE_CR_COOP_UNITS
-#define MOE_CR_COOP_UNITS 8
-#endif
-constexpr int kCoThreads = 1024, kCoUnits = MOE_CR_COOP_UNITS, kCoTable = 4096;
+constexpr int kCoThreads = 1024, kCoUnits = 8, kCoTable = 4096;
 template <CombMode MODE>
 __device__ __forceinline__ void combine_tokens_coop(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
                                                     const int* __restrict__ idx, const int* __restrict__ send_pos,
@@ -458,10 +444,7 @@ __global__ __launch_bounds__(kCoThreads) void k_comb_pull(Dims D, Ws W, const ui
 // larger k takes the groups one after another, loading each group's
 // members kSlotGroup at a time.  Either way every slot row is read once.
 constexpr int kSpWaves = kSendPartialShape.waves, kSpThreads = kSendPartialShape.threads();
-#ifndef MOE_SEND_PIECES
-#define MOE_SEND_PIECES 2
-#endif
-constexpr int kSendPieces = MOE_SEND_PIECES;
+constexpr int kSendPieces = 2;
 __global__ __launch_bounds__(kSpThreads) void k_comb_send_partial_tokens(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                    const int* __restrict__ idx,
                                                                    const int* __restrict__ send_pos,
@@ -559,96 +542,6 @@ __global__ __launch_bounds__(kSpThreads) void k_comb_send_partial_tokens(Dims D,
   }
 }
 
-// Plain streaming copy: each workgroup copies one contiguous chunk, every
-// lane with kCopyUnroll loads in flight.  On a 1 GiB copy with one
-// 1024-thread workgroup per CU, 16 loads per lane measured 6.1 TB/s against
-// 6.0 (8), 5.8 (4) and 5.75 (32): the fastest pattern found, and so the
-// ceiling the row kernels are compared with.
-constexpr int kCopyUnroll = 16;
-__global__ __launch_bounds__(kCpThreads) void k_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                        int64_t n) {
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  constexpr int U = kCopyUnroll;
-  int64_t i = b0 + threadIdx.x;
-  for (; i + (U - 1) * kCpThreads < b1; i += U * kCpThreads) {
-    v4u r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = ld16(src + i + u * kCpThreads);
-#pragma unroll
-    for (int u = 0; u < U; ++u) st16(dst + i + u * kCpThreads, r[u]);
-  }
-  for (; i < b1; i += kCpThreads) st16(dst + i, ld16(src + i));
-}
-
-// Plain streams with the access patterns of the pack and of the receive-side
-// sum, free of their row lookups and arithmetic (measurement aids, as
-// k_copy16): each workgroup a contiguous chunk of units, every thread with
-// all the loads of several units issued together (the fan-out's units past
-// the chunk repeat its last one and store nothing; the reduction's skip
-// their loads, which measured 3.5% faster for it).
-//   fan-out: unit i reads 32 bytes (src units 2i, 2i+1: a lane's 16 bf16
-//            elements) and stores their XOR at dst unit j*n + i for each
-//            j < K (the k fp8 rows);
-//   reduce:  unit i reads src units j*n + i, j < K (the k slot rows), and
-//            stores their XOR at dst unit i.
-// Units per thread: 4 for the fan-out (8 loads); for the reduction 32/K
-// (32 loads), at most 8: the fastest counts found for plain kernels of
-// these shapes.  (At K = 8 the compiler keeps two of the 16-byte values in
-// scratch; that form measured as fast as a spill-free one.)
-template <int K>
-__global__ __launch_bounds__(kCpThreads) void k_stream_fanout(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                              int64_t n) {
-  constexpr int U = 4;
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)U * kCpThreads) {
-    v4u a[U], b[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = min(i0 + (int64_t)u * kCpThreads, b1 - 1);
-      a[u] = ld16(src + 2 * i);
-      b[u] = ld16(src + 2 * i + 1);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
-      if (i < b1) {
-        const v4u q = a[u] ^ b[u];
-#pragma unroll
-        for (int j = 0; j < K; ++j) st16(dst + j * n + i, q);
-      }
-    }
-  }
-}
-
-constexpr int stream_reduce_units(int K) { return K <= 3 ? 8 : (K == 4 ? 6 : 32 / K); }   // units per thread
-
-template <int K>
-__global__ __launch_bounds__(kCpThreads) void k_stream_reduce(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                              int64_t n) {
-  constexpr int U = stream_reduce_units(K);
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)U * kCpThreads) {
-    v4u v[U][K];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
-#pragma unroll
-      for (int j = 0; j < K; ++j) v[u][j] = i < b1 ? ld16(src + j * n + i) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v4u q = v[u][0];
-#pragma unroll
-      for (int j = 1; j < K; ++j) q ^= v[u][j];
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
-      if (i < b1) st16(dst + i, q);
-    }
-  }
-}
-
-#ifndef MOE_CS_COOP
-#define MOE_CS_COOP 1
-#endif
 // The send-side partial sums with the whole workgroup on a chunk of
 // consecutive tokens (the plain copy's pattern, as k_comb_send): each slot's
 // expert-major row, weight, destination rank and, for a group leader, its
@@ -656,13 +549,7 @@ __global__ __launch_bounds__(kCpThreads) void k_stream_reduce(v4u* __restrict__ 
 // units t, t + kPsThreads, ... of every group row of the chunk's tokens,
 // each from the same 16 bytes of the group's member rows, summed in slot
 // order exactly as k_comb_send_partial does.
-#ifndef MOE_SP_COOP_PAIR
-#define MOE_SP_COOP_PAIR 1
-#endif
-#ifndef MOE_SP_COOP_UNITS
-#define MOE_SP_COOP_UNITS 8
-#endif
-constexpr int kPsThreads = 1024, kPsUnits = MOE_SP_COOP_UNITS, kPsTable = 2048, kPsPair = MOE_SP_COOP_PAIR;
+constexpr int kPsThreads = 1024, kPsUnits = 8, kPsTable = 2048, kPsPair = 1;
 __global__ __launch_bounds__(kPsThreads) void k_comb_send_partial(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                                        const int* __restrict__ idx,
                                                                        const int* __restrict__ send_pos,
@@ -764,15 +651,12 @@ __global__ __launch_bounds__(kPsThreads) void k_comb_send_partial(Dims D, Ws W, 
   }
 }
 
-#ifndef MOE_CS_COOP_MIN_ROWS
-#define MOE_CS_COOP_MIN_ROWS 131072
-#endif
-constexpr int64_t kCcMinRows = MOE_CS_COOP_MIN_ROWS;   // rows from which the cooperative form is used
+constexpr int64_t kCcMinRows = 131072;   // rows from which the cooperative form is used
 
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
-  if (MOE_CS_COOP && (int64_t)D.rows >= kCcMinRows) {
+  if ((int64_t)D.rows >= kCcMinRows) {
     const int64_t need = ((int64_t)D.rows * (D.H / 8) + kCcThreads * kCcUnroll - 1) / (kCcThreads * kCcUnroll);
     const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
     return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCcThreads), 0, st, D, W, y, row_src, comb);
@@ -781,23 +665,17 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
   return launch("k_comb_send_rows", k_comb_send_rows, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
 }
 
-#ifndef MOE_CR_COOP
-#define MOE_CR_COOP 1
-#endif
-#ifndef MOE_CR_COOP_PER_CU
-#define MOE_CR_COOP_PER_CU 1
-#endif
 constexpr int64_t kCoMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
 static int coop_grid(const Dims& D, int cus) {
   const int64_t need = ((int64_t)D.N * D.T * (D.H / 8) + kCoThreads * kCoUnits - 1) / (kCoThreads * kCoUnits);
-  const int64_t cap = (int64_t)cus * MOE_CR_COOP_PER_CU;
+  const int64_t cap = cus;   // one workgroup per CU
   return (int)(need < cap ? (need < 1 ? 1 : need) : cap);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  if (MOE_CR_COOP && (int64_t)D.N * D.T >= kCoMinTokens)
+  if ((int64_t)D.N * D.T >= kCoMinTokens)
     return launch("k_comb_recv", k_comb_recv, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, Ws{}, comb,
                   send_pos, w, out);
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
@@ -807,25 +685,19 @@ int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, c
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  if (MOE_CR_COOP && (int64_t)D.N * D.T >= kCoMinTokens)
+  if ((int64_t)D.N * D.T >= kCoMinTokens)
     return launch("k_comb_pull", k_comb_pull, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, W, y, idx,
                   send_pos, w, out);
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
   return launch("k_comb_pull_tokens", k_comb_pull_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
-#ifndef MOE_SP_COOP
-#define MOE_SP_COOP 1
-#endif
-#ifndef MOE_SP_COOP_MIN_TOKENS
-#define MOE_SP_COOP_MIN_TOKENS 16384
-#endif
-constexpr int64_t kPsMinTokens = MOE_SP_COOP_MIN_TOKENS;   // tokens (N*T) from which the cooperative form is used
+constexpr int64_t kPsMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
 
 int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                              const float* w, uint16_t* comb, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  if (MOE_SP_COOP && (int64_t)D.N * D.T >= kPsMinTokens) {
+  if ((int64_t)D.N * D.T >= kPsMinTokens) {
     const int64_t need = ((int64_t)D.N * D.T * (D.H / 8) + kPsThreads * kPsUnits - 1) / (kPsThreads * kPsUnits);
     const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
     return launch("k_comb_send_partial", k_comb_send_partial, dim3(grid), dim3(kPsThreads), 0, st, D, W, y,
@@ -842,39 +714,6 @@ int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, c
   const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
   return launch("k_comb_recv_partial", k_comb_recv_partial, dim3(grid), dim3(kCrThreads), 0, st, D, W, comb, idx,
                 send_pos, out);
-}
-
-int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st) {
-  if (n16 == 0) return MOE_OK;
-  const int grid = stream_grid(kCopyShape, cus, n16, (int64_t)kCpThreads * kCopyUnroll);
-  return launch("k_copy16", k_copy16, dim3(grid), dim3(kCpThreads), 0, st, reinterpret_cast<v4u*>(dst),
-                reinterpret_cast<const v4u*>(src), n16);
-}
-
-template <int K>
-static int launch_stream_k(int pattern, v4u* dst, const v4u* src, int64_t n16, int cus, hipStream_t st) {
-  const int64_t per_block = (int64_t)kCpThreads * (pattern == kStreamFanout ? 4 : stream_reduce_units(K));
-  const int grid = stream_grid(kCopyShape, cus, n16, per_block);
-  if (pattern == kStreamFanout)
-    return launch("k_stream_fanout", k_stream_fanout<K>, dim3(grid), dim3(kCpThreads), 0, st, dst, src, n16);
-  return launch("k_stream_reduce", k_stream_reduce<K>, dim3(grid), dim3(kCpThreads), 0, st, dst, src, n16);
-}
-
-int launch_stream(int pattern, int k, void* dst, const void* src, int64_t n16, int cus, hipStream_t st) {
-  if (n16 == 0) return MOE_OK;
-  v4u* d = reinterpret_cast<v4u*>(dst);
-  const v4u* s = reinterpret_cast<const v4u*>(src);
-  switch (k) {
-    case 1: return launch_stream_k<1>(pattern, d, s, n16, cus, st);
-    case 2: return launch_stream_k<2>(pattern, d, s, n16, cus, st);
-    case 3: return launch_stream_k<3>(pattern, d, s, n16, cus, st);
-    case 4: return launch_stream_k<4>(pattern, d, s, n16, cus, st);
-    case 5: return launch_stream_k<5>(pattern, d, s, n16, cus, st);
-    case 6: return launch_stream_k<6>(pattern, d, s, n16, cus, st);
-    case 7: return launch_stream_k<7>(pattern, d, s, n16, cus, st);
-    case 8: return launch_stream_k<8>(pattern, d, s, n16, cus, st);
-    default: return MOE_EINVAL;
-  }
 }
 
 }  // namespace moe

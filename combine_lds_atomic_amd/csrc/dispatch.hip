@@ -12,8 +12,7 @@
 //             the exchanged counts alone and copies it out of the
 //             source-major receive region; one 1024-thread workgroup per CU,
 //             its rows copied as one thread-interleaved range of 16-byte
-//             units.  (k_unpack_rows, one wave per row, remains for
-//             builds with MOE_UNPACK_COOP=0.)
+//             units.
 //   k_pack_direct  k_pack storing each row at its expert-major row instead
 //             (peers mapped into each other's memory push straight into the
 //             grouped-GEMM layout; on one GPU every rank is such a peer), so
@@ -24,39 +23,25 @@
 
 #include "route_dev.h"
 
-// fp32 -> e4m3fn conversion.  Both variants give the same bytes on the
-// whole input domain (every bfloat16 pair x <= amax), which the exhaustive
-// sweep test checks against the oracle:
-//   MOE_PACK_CVT 0: round with integer operations on the float's bits;
-//                1: v_cvt_pk_fp8_f32 (on gfx950 it converts to OCP e4m3fn,
-//                   round to nearest even), two values per instruction.
-#ifndef MOE_PACK_CVT
-#define MOE_PACK_CVT 1
-#endif
-#ifndef MOE_PACK_PASSES
-#define MOE_PACK_PASSES 4
-#endif
 
 namespace moe {
 
 constexpr int kPkWaves = kPackShape.waves, kPkThreads = kPackShape.threads();
 constexpr int kPackCols = kWave * 16;         // elements one wave covers per pass (16 per lane)
-constexpr int kPackPasses = MOE_PACK_PASSES;  // passes whose loads are issued together
+constexpr int kPackPasses = 4;                // passes whose loads are issued together
 
 // Four quotients x[i] / scale (IEEE division) packed as e4m3fn bytes,
-// little end first.
+// little end first.  v_cvt_pk_fp8_f32 converts two floats to OCP e4m3fn
+// (round to nearest even, saturating) per instruction on gfx950; the
+// exhaustive sweep test checks its bytes against the oracle's encoder on
+// every bfloat16 pair x <= amax.
 __device__ __forceinline__ uint32_t quant4(const float* v, float scale) {
   float q[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) q[i] = v[i] / scale;
-#if MOE_PACK_CVT
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
   return (uint32_t)w;
-#else
-  return f32_to_e4m3fn(q[0]) | (f32_to_e4m3fn(q[1]) << 8) | (f32_to_e4m3fn(q[2]) << 16) |
-         (f32_to_e4m3fn(q[3]) << 24);
-#endif
 }
 
 // This lane's 16 elements of each pass of the chunk starting at column c0
@@ -163,15 +148,6 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
   pack_scales(D, h0, h1, row, lane, recv_s, ssw);
 }
 
-// MOE_PACK_PRELOAD: k_pack issues a work item's first token loads before it
-// resolves the item's rows, so the two latencies overlap.  Measured in one
-// process: 2-3 us less at the decode shape, no change from combine-heavy
-// size up (where the kernel runs at 98 VGPRs, 4 workgroups per CU, against
-// 65 VGPRs and 7 without it).  Staging the routing tables in LDS as the
-// unpack does changed nothing here and was left out.
-#ifndef MOE_PACK_PRELOAD
-#define MOE_PACK_PRELOAD 1
-#endif
 
 // The row slot i (of rank s's T*k) is packed to, -1 for none.  DIRECT =
 // false: its source-major receive row; DIRECT = true: its expert-major row,
@@ -233,18 +209,17 @@ __device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const ui
     int tok, sl, h0, h1;
     item_cols(D, item, tok, sl, h0, h1);
     const int s = tok / D.T, t = tok - s * D.T;
-#if MOE_PACK_PRELOAD
+    // The item's first token loads go out before its rows are resolved, so
+    // the two latencies overlap: 2-3 us less at the decode shape, no change
+    // from combine-heavy size up (98 VGPRs, 4 workgroups per CU there,
+    // against 65 and 7 without).  Staging the routing tables in LDS as the
+    // unpack does changed nothing here.
     v4u a[kPackPasses], b[kPackPasses];
     if (x != nullptr) load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
-#endif
     // Lane j < k resolves slot j.
     const int row = lane < D.k ? pack_slot_row<DIRECT>(D, W, idx, send_pos, row_src, s, t * D.k + lane, sl == 0) : -1;
     if (x == nullptr) continue;
-#if MOE_PACK_PRELOAD
     pack_item<true>(D, item, row, x, recv_q, recv_s, sscale[wv], a, b);
-#else
-    pack_item<false>(D, item, row, x, recv_q, recv_s, sscale[wv]);
-#endif
   }
 }
 
@@ -801,20 +776,8 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll_direct(Dims D, Ws W, c
   dispatch_ll<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off, npack);
 }
 
-constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
-// k_unpack_rows launch form (waves per workgroup x workgroups per CU, 16-B
-// loads per lane issued together while copying a row), used only by builds
-// with MOE_UNPACK_COOP=0: the cooperative k_unpack measured equal at the
-// decode shape and faster everywhere else (tiny 21 against 25 us, Kimi
-// dispatch 199-201 against 205-213, combine-heavy and prefill 4-7%).
-constexpr LaunchShape kUnpackRowsShape = MOE_UNPACK_SHAPE;
-constexpr int kUnpackRowsUnroll = 8;
-
-// Staging of one region's routing tables in LDS (the unpack kernels): the searches
+// Staging of one region's routing tables in LDS (the unpack kernel): the searches
 // that map an expert-major row to its segment then read no global memory.
-#ifndef MOE_UNPACK_STAGE
-#define MOE_UNPACK_STAGE 1
-#endif
 constexpr int kStageInts = 2 * kMaxE + (kMaxE + kMaxN) + (kMaxE + 1) + (kMaxN + 1);
 
 // One region's routing tables staged in LDS, for the row searches.
@@ -837,7 +800,7 @@ __device__ __forceinline__ UnpackStage unpack_stage(const Dims& D, const Ws& W, 
   S.so = S.sie + (N + 1) * L;
   S.eo = S.so + N * (L + 1);
   S.ro = S.eo + (L + 1);
-  S.d0 = MOE_UNPACK_STAGE && lo < hi ? floor_index(svp, N + 1, lo) : -1;
+  S.d0 = lo < hi ? floor_index(svp, N + 1, lo) : -1;
   if (S.d0 >= 0) {
     const int d0 = S.d0;
     for (int i = threadIdx.x; i < (N + 1) * L; i += THREADS) S.sie[i] = W.src_in_exp[(i / L) * E + d0 * L + i % L];
@@ -891,57 +854,15 @@ __device__ __forceinline__ void unpack_row(const Dims& D, const Ws& W, const Unp
   }
 }
 
-template <int WAVES, int UNROLL>
-__global__ __launch_bounds__(WAVES * kWave) void k_unpack_rows(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
-                                                       const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
-                                                       float* __restrict__ x_s, int* __restrict__ exp_off,
-                                                       int* __restrict__ row_src) {
-  constexpr int kT = WAVES * kWave;
-  __shared__ int svp[kMaxN + 1];
-  __shared__ int stage[kStageInts];
-  for (int i = threadIdx.x; i <= D.N; i += kT) svp[i] = W.vprefix[i];
-  if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kT) exp_off[i] = W.exp_off[i];
-  __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const bool scales16 = (D.NB & 3) == 0;   // scale rows are whole 16-byte units
-  int lo, hi;
-  block_range(svp[D.N], lo, hi);        // valid rows, in region order
-  const UnpackStage S = unpack_stage<kT>(D, W, svp, stage, lo, hi);
-  for (int g0 = lo + wv; g0 < hi; g0 += WAVES * kRowsPerPass) {
-    int src = -1, dst = -1;
-    const int g = g0 + lane * WAVES;
-    if (lane < kRowsPerPass && g < hi) unpack_row(D, W, S, svp, g, row_src, src, dst);
-    if (x_q == nullptr) continue;   // layout only
-    for (int r = 0; r < kRowsPerPass; ++r) {
-      const int sr = __builtin_amdgcn_readlane(src, r);
-      const int dr = __builtin_amdgcn_readlane(dst, r);
-      if (sr < 0 || dr < 0) continue;
-      wave_copy16<UNROLL>(reinterpret_cast<v4u*>(x_q + (int64_t)dr * D.H),
-                     reinterpret_cast<const v4u*>(recv_q + (int64_t)sr * D.H), D.H / 16, lane);
-      if (scales16) {
-        const int n16 = D.NB / 4;
-        if (lane < n16)
-          st16(reinterpret_cast<v4u*>(x_s + (int64_t)dr * D.NB) + lane,
-               ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)sr * D.NB) + lane));
-        for (int c = lane + kWave; c < n16; c += kWave)
-          st16(reinterpret_cast<v4u*>(x_s + (int64_t)dr * D.NB) + c,
-               ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)sr * D.NB) + c));
-      } else {
-        for (int c = lane; c < D.NB; c += kWave) x_s[(int64_t)dr * D.NB + c] = recv_s[(int64_t)sr * D.NB + c];
-      }
-    }
-  }
-}
-
-// The same unpack with the whole workgroup on consecutive rows (the access
+// The unpack, with the whole workgroup on consecutive rows (the access
 // pattern of the plain copy, as k_comb_send): per chunk of rows, their
 // sources are resolved into LDS, then thread t copies the chunk's 16-byte
 // payload units t, t + kUcThreads, ... (kUcUnroll per step, loads before
 // stores) and its scale units likewise.  Measured in one process,
-// alternating calls, against the per-row large form: combine-heavy 1307-1402
-// against 1403-1461 us, prefill 2633-2697 against 2776-2840.  (Sixteen
-// units per thread would spill at this workgroup size.)
+// alternating calls, against a form with one wave per row: combine-heavy
+// 1307-1402 against 1403-1461 us, prefill 2633-2697 against 2776-2840, equal
+// at the decode shape, tiny 21 against 25 us, Kimi dispatch 199-201 against
+// 205-213.  (Sixteen units per thread would spill at this workgroup size.)
 constexpr int kUcThreads = 1024, kUcUnroll = 8;
 constexpr int kUcMaxRows = kUcThreads * kUcUnroll / (kScaleBlock / 16);   // rows per chunk at H = 128
 __global__ __launch_bounds__(kUcThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
@@ -1047,32 +968,20 @@ int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, 
   return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
 }
 
-#ifndef MOE_UNPACK_COOP
-#define MOE_UNPACK_COOP 1
-#endif
-
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
-  if (MOE_UNPACK_COOP) {
-    const int64_t need = ((int64_t)D.rows * (D.H / 16) + kUcThreads * kUcUnroll - 1) / (kUcThreads * kUcUnroll);
-    const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
-    return launch("k_unpack", k_unpack, dim3(grid), dim3(kUcThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s,
-                  exp_off, row_src);
-  }
-  constexpr LaunchShape S = kUnpackRowsShape;
-  const int grid = stream_grid(S, cus, (int64_t)D.rows, S.waves);
-  return launch("k_unpack_rows", k_unpack_rows<S.waves, kUnpackRowsUnroll>, dim3(grid), dim3(S.threads()), 0, st, D,
-                W, recv_q, recv_s, x_q, x_s, exp_off, row_src);
+  const int64_t need = ((int64_t)D.rows * (D.H / 16) + kUcThreads * kUcUnroll - 1) / (kUcThreads * kUcUnroll);
+  const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
+  return launch("k_unpack", k_unpack, dim3(grid), dim3(kUcThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
+                row_src);
 }
 
 // Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic
-// LDS: what the occupancy query allows, at most MOE_LL_BLOCKS_PER_CU.  On
-// MI355X the first wave of this launch holds 6 per CU although the query
-// reports 7; with 7 per CU every 7th packer starts only after another has
-// finished, which costs more than it gains (measured at the decode shapes).
-#ifndef MOE_LL_BLOCKS_PER_CU
-#define MOE_LL_BLOCKS_PER_CU 6
-#endif
+// LDS: what the occupancy query allows, at most kLlBlocksPerCu.  On MI355X
+// the first wave of this launch holds 6 per CU although the query reports 7;
+// with 7 per CU every 7th packer starts only after another has finished,
+// which costs more than it gains (measured at the decode shapes).
+constexpr int kLlBlocksPerCu = 6;
 static int ll_blocks_per_cu(const void* kernel, size_t lds) {
   static std::mutex mu;
   static std::map<std::tuple<int, const void*, size_t>, int> cache;
@@ -1083,7 +992,7 @@ static int ll_blocks_per_cu(const void* kernel, size_t lds) {
   if (it != cache.end()) return it->second;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, lds) != hipSuccess || nb < 1) nb = 1;
-  if (nb > MOE_LL_BLOCKS_PER_CU) nb = MOE_LL_BLOCKS_PER_CU;
+  if (nb > kLlBlocksPerCu) nb = kLlBlocksPerCu;
   cache[{dev, kernel, lds}] = nb;
   return nb;
 }

@@ -171,24 +171,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// float32 -> OCP E4M3 (e4m3fn) byte, round to nearest even, saturating to
-// +-448; NaN -> S.1111.111.  Bit manipulation on the IEEE pattern.
-__device__ __forceinline__ uint32_t f32_to_e4m3fn(float q) {
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;        // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;       // >= 448: RNE gives 448 up to 464, saturate above
-  if (a < 0x3C800000u) {                           // below 2^-6: subnormal spacing 2^-9
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
-    return sign | (uint32_t)m;                     // m == 8 is the smallest normal, 0x08
-  }
-  // Normal range: keep 3 of the 23 mantissa bits, ties to even; a carry
-  // moves into the exponent.  Rebias 127 -> 7.
-  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-  return sign | (r - (120u << 3));
-}
-
 // Row inside region d of block index u of source s's rows for d (u =
 // send_pos - send_off[s][d*L]), given recv_off[d][s]: the sender's early
 // rows first, then its share of the region's common part.
@@ -206,34 +188,16 @@ __device__ __forceinline__ int region_row(const Dims& D, int s, int u, int recv_
 // per workgroup, workgroups per CU), measured on the combine-heavy workload.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-#ifndef MOE_NONTEMPORAL
-#define MOE_NONTEMPORAL 1
-#endif
 
 struct LaunchShape {
   int waves;          // waves per workgroup
   int blocks_per_cu;  // workgroups per CU in the grid
   constexpr int threads() const { return waves * 64; }
 };
-#ifndef MOE_PACK_SHAPE
-#define MOE_PACK_SHAPE {4, 8}
-#endif
-#ifndef MOE_UNPACK_SHAPE
-#define MOE_UNPACK_SHAPE {16, 1}
-#endif
-#ifndef MOE_COMB_SEND_SHAPE
-#define MOE_COMB_SEND_SHAPE {8, 2}
-#endif
-#ifndef MOE_COMB_RECV_SHAPE
-#define MOE_COMB_RECV_SHAPE {4, 8}
-#endif
-constexpr LaunchShape kPackShape = MOE_PACK_SHAPE;
-constexpr LaunchShape kCombSendShape = MOE_COMB_SEND_SHAPE;
-#ifndef MOE_SEND_PARTIAL_SHAPE
-#define MOE_SEND_PARTIAL_SHAPE {16, 1}
-#endif
-constexpr LaunchShape kCombRecvShape = MOE_COMB_RECV_SHAPE;
-constexpr LaunchShape kSendPartialShape = MOE_SEND_PARTIAL_SHAPE;
+constexpr LaunchShape kPackShape = {4, 8};
+constexpr LaunchShape kCombSendShape = {8, 2};
+constexpr LaunchShape kCombRecvShape = {4, 8};
+constexpr LaunchShape kSendPartialShape = {16, 1};
 constexpr LaunchShape kCopyShape = {16, 1};
 
 // Grid of a streaming kernel of shape S over `items` work units, at most
@@ -244,20 +208,10 @@ inline int stream_grid(LaunchShape S, int cus, int64_t items, int64_t per_block)
   return (int)(need < 1 ? 1 : (need < cap ? need : cap));
 }
 
-__device__ __forceinline__ v4u ld16(const v4u* p) {
-#if MOE_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-__device__ __forceinline__ void st16(v4u* p, v4u v) {
-#if MOE_NONTEMPORAL
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
+// Non-temporal on both sides: 3-4% faster than plain accesses on the row
+// kernels, and the fastest of the cache-policy combinations on a copy.
+__device__ __forceinline__ v4u ld16(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st16(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
 // This workgroup's share [lo, hi) of n items split evenly over the grid.
 __device__ __forceinline__ void block_range(int n, int& lo, int& hi) {
@@ -318,9 +272,6 @@ int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, cons
                              const float* w, uint16_t* comb, int cus, hipStream_t st);
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
                              uint16_t* out, int cus, hipStream_t st);
-int launch_copy(void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
-constexpr int kStreamFanout = 1, kStreamReduce = 2;   // moe_stream patterns (MOE_STREAM_*)
-int launch_stream(int pattern, int k, void* dst, const void* src, int64_t n16, int cus, hipStream_t st);
 int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st);
 
 }  // namespace moe

@@ -322,33 +322,6 @@ int moe_status(void *ws, void *stream, uint32_t *flags);
 int moe_layout_export(const moe_shape *shape, const void *ws, int32_t *cnt, int32_t *send_off, int32_t *recv_off,
                       int32_t *recv_total, int32_t *base, void *stream);
 
-/*
- * Measurement aid, not part of dispatch / combine: a plain streaming copy of
- * nbytes (multiple of 16, both pointers 16-B aligned) with the same 16-byte
- * accesses the row kernels use.  It gives the achievable read+write HBM rate
- * next to the roofline and calibrates the hardware byte counters.
- */
-int moe_copy(void *dst, const void *src, int64_t nbytes, void *stream);
-
-/*
- * Measurement aid, not part of dispatch / combine: plain streams with the
- * access patterns of two phases, free of their row lookups and arithmetic,
- * giving each phase's achievable HBM rate on the same GPU.  n16 counts
- * 16-byte units; k in [1, 8]; both pointers 16-B aligned, caller-owned
- * device memory; what is stored is the XOR of the bytes read.
- *   MOE_STREAM_FANOUT: unit i reads 32 bytes (src units 2i and 2i+1) and
- *     stores 16 bytes at dst unit j*n16 + i for every j < k: the dispatch
- *     pack's bf16 row in, k fp8 rows out.  src holds 2*n16 units, dst k*n16.
- *   MOE_STREAM_REDUCE: unit i reads src units j*n16 + i for every j < k and
- *     stores 16 bytes at dst unit i: the receive-side sum's k rows in, one
- *     out.  src holds k*n16 units, dst n16.
- * Errors: MOE_EINVAL for another pattern, k outside [1, 8] or n16 < 0;
- * MOE_ERANGE for n16 above 2^40 (16 TiB); MOE_ENULL / MOE_EALIGN.
- */
-#define MOE_STREAM_FANOUT 1
-#define MOE_STREAM_REDUCE 2
-int moe_stream(int pattern, int k, void *dst, const void *src, int64_t n16, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -1,6 +1,7 @@
 /*
  * The C ABI from plain C: compiled by tests/test_c_abi.py with gcc -std=c99
- * against include/moe_ep.h alone and linked to the built libmoe_ep.so.  It
+ * against include/moe_ep.h and include/moe_streams.h, linked to the built
+ * libmoe_ep.so and libmoe_streams.so.  It
  * calls only the sizing functions and argument checks that return before
  * anything is enqueued, so it needs no GPU.  Prints one line per failed
  * check; the exit status is the number of failures.
@@ -9,6 +10,7 @@
 #include <stdio.h>
 
 #include "moe_ep.h"
+#include "moe_streams.h"
 
 static int fails = 0;
 

@@ -110,6 +110,23 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     fl = ctypes.c_uint32()
     assert lib.moe_status(None, None, ctypes.byref(fl)) == -2
     assert lib.moe_status(_p(A + 4), None, ctypes.byref(fl)) == -3
+    assert lib.moe_layout_export(s, None, None, None, None, None, None, None) == -2
+
+
+def test_streams_library_exports_and_rejections():
+    """libmoe_streams (include/moe_streams.h), the benchmark's plain streams,
+    is a library of its own: it exports what its header declares, and
+    libmoe_ep exports none of it."""
+    from combine_lds_atomic_amd import streams as S
+    txt = open(S.HEADER).read()
+    declared = set(re.findall(r"^\s*int\s+(moe_\w+)\s*\(", txt, re.M))
+    assert declared == {"moe_copy", "moe_stream"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in nm.splitlines() if " T " in ln}
+    assert declared <= exported and not [x for x in exported if x.startswith("moe_") and x not in declared]
+    assert not declared & set(moe.declared_symbols())
+    A = 0x10000000
+    lib = S.lib
     assert lib.moe_copy(_p(A), _p(A), 17, None) == -1
     assert lib.moe_copy(_p(A + 1), _p(A), 16, None) == -3
     assert lib.moe_stream(3, 8, _p(A), _p(A), 16, None) == -1          # no such pattern
@@ -120,4 +137,3 @@ def test_null_and_alignment_rejections_happen_on_the_host():
     assert lib.moe_stream(2, 8, _p(A), _p(A), (1 << 40) + 1, None) == -4   # above 2^40 units
     assert lib.moe_stream(1, 8, None, _p(A), 16, None) == -2
     assert lib.moe_stream(1, 8, _p(A), _p(A + 8), 16, None) == -3
-    assert lib.moe_layout_export(s, None, None, None, None, None, None, None) == -2

@@ -1,6 +1,7 @@
-"""The C ABI is usable from plain C: include/moe_ep.h compiles as C99 with
-warnings as errors, and a C program linked to libmoe_ep.so gets the sizes
-and host-side rejections the header documents (no GPU needed)."""
+"""The C ABI is usable from plain C: include/moe_ep.h (and the benchmark's
+include/moe_streams.h) compile as C99 with warnings as errors, and a C
+program linked to the libraries gets the sizes and host-side rejections the
+headers document (no GPU needed)."""
 import os
 import shutil
 import subprocess
@@ -17,7 +18,7 @@ def test_c_program_against_the_header(tmp_path):
     exe = tmp_path / "c_abi_check"
     libdir = os.path.dirname(moe.LIB_PATH)
     cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
-           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), f"-L{libdir}", "-lmoe_ep",
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), f"-L{libdir}", "-lmoe_ep", "-lmoe_streams",
            f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr

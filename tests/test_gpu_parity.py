@@ -247,6 +247,72 @@ def test_fixed_region_overflow_is_flagged_and_contained():
         assert (rs[a:a + lay.recv_total[d]] == want[a:a + lay.recv_total[d]]).all()
 
 
+def test_combine_sums_in_slot_order():
+    """Rows of 2^24, 1 and -2^24 whose float32 sum depends on the order of the
+    additions (tests/golden/combine_slot_order.json): combine send + recv and
+    the pulling combine give the slot-order sums."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "combine_slot_order.json")) as f:
+        g = json.load(f)
+    idx = np.array(g["idx"], np.int32)
+    w = np.array(g["w"], np.float32)
+    cfg = _small("slot_order", N=g["N"], T=g["T"], H=g["H"], E=g["E"], k=g["k"])
+    lay = O.layout(idx, cfg.E, cfg.N)
+    vals = np.array(g["y_slot_values"], np.float32)
+    y = np.zeros((lay.total_rows, cfg.H), np.float32)
+    for s in range(cfg.N):
+        for t in range(cfg.T):
+            for j in range(cfg.k):
+                y[lay.em_row[s, t, j]] = vals[s, t, j]
+    y_d = torch.from_numpy(y).to(torch.bfloat16).cuda()
+    r = run_all(cfg, cfg.T, idx=idx, w=w, y=y_d, payload=False)
+    check_full(r, lay)
+    got = O.bf16_from_bits(bf16_np(r["B"].out)).astype(np.float64)
+    assert (got == np.array(g["out_slot_order"])[:, :, None]).all()
+
+
+@pytest.mark.parametrize("region_rows", [0, 700])
+def test_combine_reuses_dispatch_buffers(region_rows):
+    """Buffers are reused between dispatch and combine: once moe_dispatch_recv
+    has run, combine send writes `comb` into the memory that held the fp8
+    receive regions, and combine recv writes `out` over the token rows."""
+    import combine_lds_atomic_amd as moe
+    cfg = _small("reuse", N=4, T=96, H=384, E=16, k=4)
+    T = cfg.T
+    idx, w = W.routing(cfg, T)
+    lay = O.layout(idx, cfg.E, cfg.N, region_rows)
+    sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k, region_rows)
+    B = moe.allocate(sh, "cuda", payload=True, combine=False, fill_rows=0x5A)
+    rows = B.rows
+    comb_bytes = cfg.N * T * cfg.k * cfg.H * 2
+    pool = torch.full((max(rows * cfg.H, comb_bytes),), 0x5A, dtype=torch.uint8, device="cuda")
+    recv_q = pool[:rows * cfg.H].view(rows, cfg.H)
+    x = W.tokens(cfg, "cuda", T)
+    x_host = x.float().cpu().numpy()
+    idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    moe.moe_dispatch_send(sh, x, idx_d, recv_q, B.recv_s, B.send_pos, B.ws)
+    moe.moe_dispatch_recv(sh, recv_q, B.recv_s, B.ws, B.x_q, B.x_s, B.exp_off, B.row_src)
+    comb = pool[:comb_bytes].view(torch.bfloat16).view(cfg.N, T * cfg.k, cfg.H)   # recv_q's memory
+    out = x                                                                          # the tokens' memory
+    y = W.expert_outputs(cfg, rows, "cuda")
+    moe.moe_combine_send(sh, y, B.row_src, B.ws, comb)
+    moe.moe_combine_recv(sh, comb, B.send_pos, w_d, out)
+    assert moe.moe_status(B.ws) == lay.flags
+    rq, rs = O.dispatch_send(x_host, lay)
+    xq, xs, rsrc = O.dispatch_recv(rq, rs, lay)
+    erow = lay.em_row[lay.em_row >= 0]
+    assert (B.x_q.cpu().numpy()[erow] == xq[erow]).all()
+    assert (B.x_s.cpu().numpy()[erow].view(np.uint32) == xs[erow].view(np.uint32)).all()
+    assert (B.row_src.cpu().numpy()[erow] == rsrc[erow]).all()
+    yb = bf16_np(y)
+    comb_o = O.combine_send(yb, rsrc, cfg.N, T, cfg.k)
+    got_comb = bf16_np(comb).reshape(-1, cfg.H)
+    wr = rsrc[rsrc >= 0]
+    assert (got_comb[wr] == comb_o[wr]).all()
+    check_combine_out(bf16_np(out), O.combine_recv(comb_o, lay.send_pos, w, T, cfg.k))
+
+
 def test_repeat_runs_are_bitwise_identical():
     cfg = W.CONFIGS["tiny"]
     a = run_all(cfg, 128)

@@ -1,12 +1,12 @@
 """moe_stream, the plain fan-out and reduction streams that bench.py times as
 the pack's and the receive-side sum's achievable rates: every stored byte is
-the XOR its definition in include/moe_ep.h names, at sizes that leave ragged
+the XOR its definition in include/moe_streams.h names, at sizes that leave ragged
 workgroup chunks and partial unit groups."""
 import numpy as np
 import pytest
 import torch
 
-import combine_lds_atomic_amd as moe
+from combine_lds_atomic_amd import streams as moe
 
 pytestmark = pytest.mark.gpu
 
