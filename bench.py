@@ -5,32 +5,35 @@ positions, quantise + pack), moe_dispatch_recv (expert-major unpack),
 moe_combine_send and moe_combine_recv, for all N logical ranks.  Inputs are
 seeded synthetic tensors already resident in HBM.  Prints one JSON line.
 
-Workloads whose combine batch differs from the dispatch batch (the Kimi-K2
-shape: dispatch 128, combine 4096 tokens per rank) time the dispatch at the
-dispatch batch and the combine on the layout of an untimed, payload-free
-dispatch at the combine batch.
+The headline workload (default combine_heavy: T=4096, H=7168) gives the line's
+value; every other workload is measured the same way in the same run and
+reported under "workloads" (tiny, dsv3_decode, kimi_skewed, prefill,
+prefill_forced).  Workloads whose combine batch differs from the dispatch
+batch (the Kimi-K2 shape: dispatch 128, combine 4096 tokens per rank) time the
+dispatch at the dispatch batch and the combine on the layout of an untimed,
+payload-free dispatch at the combine batch.
 
-The pulling combine (moe_combine_pull) and the combine with send-side partial
-sums (moe_combine_send_partial + moe_combine_recv_partial) are timed after the
-steps, on the same data, and reported beside them; they are not part of the
-step.  So are the direct dispatch (moe_dispatch_direct, in place of send +
-recv), when every rank's slots fit one routing chunk (T*k <= 4096) its single
-launch (moe_dispatch_direct_ll) and the step with the single-launch
-moe_dispatch_send_ll in place of moe_dispatch_send (also with early rows),
-and the fastest composition of one layer (the fastest of these dispatches,
-the pulling combine) as whole steps, and cold-cache phase times (1 GiB of
-scratch written before each call).  Each phase's rate is also given as a
-fraction of its access pattern's ceiling: a plain stream of the same shape
-on the phase's own buffers (moe_stream fan-out for the pack, moe_copy for
-unpack and combine send, moe_stream reduction for the receive-side sum).  The CPU
-baselines (the oracle in one process, and in min(16, cores) processes on
-independent problems) run first, before the GPU is touched.
+Beside the step, on the same data: the pulling combine (moe_combine_pull), the
+combine with send-side partial sums, the direct dispatch (moe_dispatch_direct)
+and, when every rank's slots fit one routing chunk (T*k <= 4096), the single
+launches (moe_dispatch_send_ll, also with early rows, and
+moe_dispatch_direct_ll); the fastest composition of one layer as whole steps;
+cold-cache phase times (1 GiB of scratch written before each call).  Each
+phase's rate is also given as a fraction of two ceilings measured on the
+phase's own buffers: the HIP runtime's own device-to-device copy
+(hipMemcpyAsync) and fill (hipMemsetAsync, a write-only stream), and plain
+streams of the phase's access pattern (libmoe_streams: a fan-out for the pack,
+a copy for unpack and combine send, a reduction for the receive-side sum).
+The CPU baselines (the oracle in one process, and in min(16, cores)
+processes on independent problems) run first, before the GPU is touched.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--workloads all|none|a,b,...] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -42,22 +45,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 PHASES = ["dispatch_send", "dispatch_recv", "combine_send", "combine_recv"]
-KERNEL_OF = {"dispatch_send": "k_pack", "dispatch_recv": "k_unpack", "combine_send": "k_comb_send",
-             "combine_recv": "k_comb_recv"}
-# The library's small-problem forms: one wave per row below 131072 rows
-# (k_comb_send_rows), one wave per token below 16384 tokens
-# (k_comb_recv_tokens).
-ROWS_FORM_BELOW = 131072
-TOKENS_FORM_BELOW = 16384
+# The kernel that moves each phase's bytes (dispatch send also runs the
+# routing kernels, dispatch recv the row-map kernel k_unpack_index).
+KERNEL_OF = {"dispatch_send": "k_pack_os", "dispatch_recv": "k_unpack_os", "combine_send": "k_comb_send_os",
+             "combine_recv": "k_comb_recv_os"}
+ALL_WORKLOADS = ["tiny", "dsv3_decode", "combine_heavy", "kimi_skewed", "prefill", "prefill_forced"]
+DTYPE = "f32 arithmetic; e4m3fn payload with f32 block-128 scales (dispatch), bf16 (combine)"
 
 
-def kernel_of(phase: str, rows: int, tokens: int) -> str:
-    k = KERNEL_OF[phase]
-    if phase == "combine_send" and rows < ROWS_FORM_BELOW:
-        return k + "_rows"
-    if phase == "combine_recv" and tokens < TOKENS_FORM_BELOW:
-        return k + "_tokens"
-    return k
+def kernel_of(phase: str) -> str:
+    return KERNEL_OF[phase]
 
 
 def algorithmic_bytes(N, T, H, E, k, Tc=None, G=None):
@@ -80,6 +77,18 @@ def algorithmic_bytes(N, T, H, E, k, Tc=None, G=None):
         "combine_recv": Pc * rowb + N * Tc * H * 2 + 2 * N * Tc * k * 4,
         "combine_pull": Pc * rowb + N * Tc * H * 2 + 3 * N * Tc * k * 4,
     }
+
+
+def phase_read_write(N, T, H, E, k, Tc=None):
+    """(read bytes, written bytes) of each of the four phases; their sums are
+    algorithmic_bytes'.  The pack writes four times what it reads."""
+    Tc = T if Tc is None else Tc
+    P, Pc = N * T * k, N * Tc * k
+    rowq, rowb = H + 4 * (H // 128), 2 * H
+    return {"dispatch_send": (N * T * 2 * H + N * T * k * 4, P * rowq + N * T * k * 4 + N * E * 4),
+            "dispatch_recv": (P * rowq, P * rowq),
+            "combine_send": (Pc * rowb, Pc * rowb),
+            "combine_recv": (Pc * rowb + 2 * N * Tc * k * 4, N * Tc * H * 2)}
 
 
 def combine_groups(idx, L):
@@ -191,43 +200,47 @@ def cpu_baseline_parallel(T_sample: int, procs: int):
                       f"NumPy, input generation excluded"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="combine_heavy")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: all N logical EP ranks live in one MI355X's HBM, so --gpus {args.gpus} "
-              "is not a configuration of this benchmark (the multi-GPU sharding is a design, not built).",
-              file=sys.stderr)
-        sys.exit(2)
+class HipRuntime:
+    """The HIP runtime torch has loaded (found by soname in the process map),
+    for its own copy and fill: independent ceilings beside this repository's
+    kernels."""
+    MEMCPY_D2D = 3   # hipMemcpyDeviceToDevice
 
+    def __init__(self):
+        maps = open("/proc/self/maps").read()
+        paths = sorted({ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln})
+        if len(paths) != 1:
+            raise RuntimeError(f"expected one HIP runtime in the process, found {paths}")
+        self.lib = ctypes.CDLL(paths[0])
+        self.lib.hipMemcpyAsync.restype = ctypes.c_int
+        self.lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p]
+        self.lib.hipMemsetAsync.restype = ctypes.c_int
+        self.lib.hipMemsetAsync.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+
+    def copy(self, dst, src, nbytes, stream):
+        rc = self.lib.hipMemcpyAsync(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()), nbytes,
+                                     self.MEMCPY_D2D, ctypes.c_void_p(stream.cuda_stream))
+        if rc:
+            raise RuntimeError(f"hipMemcpyAsync returned {rc}")
+
+    def fill(self, dst, nbytes, stream):
+        rc = self.lib.hipMemsetAsync(ctypes.c_void_p(dst.data_ptr()), 0x5A, nbytes, ctypes.c_void_p(stream.cuda_stream))
+        if rc:
+            raise RuntimeError(f"hipMemsetAsync returned {rc}")
+
+
+def measure(cfg, args, dev, stream, hip):
+    """Every measurement of one workload; returns the result dict and the
+    step's total algorithmic bytes and mean step time (ms)."""
     import numpy as np
     import torch
 
     import combine_lds_atomic_amd as moe
+    from combine_lds_atomic_amd import streams as S
     import workloads as W
 
-    cfg = W.CONFIGS[args.workload]
     T, Tc = cfg.T, cfg.Tc
-    # The CPU baselines run first: the parallel one starts processes, which
-    # should happen before this process initialises the GPU.
-    cpu_single = cpu_par = None
-    if not args.no_cpu_baseline:
-        note("cpu baseline: the oracle, one process")
-        cpu_single = cpu_baseline(args.cpu_sample_tokens)
-        procs = min(16, len(os.sched_getaffinity(0)))
-        note(f"cpu baseline: the oracle, {procs} processes")
-        cpu_par = cpu_baseline_parallel(max(1, args.cpu_sample_tokens // 8), procs)
-    note(f"gpu: {cfg.name}, {args.warmup} warm-up and {args.steps} timed steps")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-
     # Dispatch problem (timed) at batch T.
     sh = moe.shape(cfg.N, T, cfg.H, cfg.E, cfg.k)
     idx, w = W.routing(cfg, T)
@@ -265,7 +278,7 @@ def main():
     torch.cuda.synchronize()
     flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
-        raise SystemExit(f"device error flags {flags:#x} during warm-up")
+        raise SystemExit(f"device error flags {flags:#x} during warm-up ({cfg.name})")
 
     # Timed region: exactly K steps, synchronised on both sides.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -306,13 +319,13 @@ def main():
 
     graph_step_ms = graph_ms(moe.moe_dispatch_send)
 
-    note("single-launch dispatch")
     # The single-launch dispatch (moe_dispatch_send_ll, one routing chunk per
     # rank only) in the same step in place of moe_dispatch_send: its phase
     # time, the eager and graph-replayed step, and a bitwise comparison of its
     # outputs with the multi-launch call's.
     single = None
     if T * cfg.k <= 4096 and T > 0:
+        note(f"{cfg.name}: single-launch dispatch")
         ref = {f: getattr(B, f).clone() for f in ("send_pos", "recv_q", "recv_s", "x_q", "x_s", "row_src")}
         for _ in range(args.warmup):
             step(send=moe.moe_dispatch_send_ll)
@@ -332,6 +345,7 @@ def main():
                   "same_bytes_as_dispatch_send": bool(same)}
         single_ms = ms_l.mean(axis=0)[0]
         single_p90 = np.percentile(ms_l[:, 0], 90)
+        del ref
 
         # The same with early rows: fixed regions that start with C private
         # rows per sender (C about 1.25x the mean rows of a rank pair), so
@@ -373,9 +387,12 @@ def main():
         early_ms = ms_e.mean(axis=0)[0]
         single["early_rows"] = {"early_rows": C, "region_rows": R, "dispatch_send": None,
                                 "same_send_pos": same_e}
+        flags_e = moe.moe_status(Be.ws)
+        if flags_e:
+            raise SystemExit(f"device error flags {flags_e:#x} in the early-row steps ({cfg.name})")
         del Be, ye, comb_e, out_e
 
-    note("direct dispatch")
+    note(f"{cfg.name}: direct dispatch")
     # The direct dispatch (moe_dispatch_direct: rows stored straight at their
     # expert-major rows, no receive regions, no unpack) on the same inputs
     # and buffers, compared bit for bit with the two-call path's outputs.
@@ -399,7 +416,7 @@ def main():
     direct_ll = time_direct(moe.moe_dispatch_direct_ll) if T * cfg.k <= 4096 and T > 0 else None
     del ref
 
-    note("pulling and partial combines")
+    note(f"{cfg.name}: pulling and partial combines")
     # The pulling combine on the same data (not part of the step).
     pull_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for _ in range(2):
@@ -430,7 +447,7 @@ def main():
     part_ms = np.array([[part_ev[i][p].elapsed_time(part_ev[i][p + 1]) for p in range(2)]
                         for i in range(args.steps)]).mean(axis=0)
     part_diff = float((out_p.view(torch.int16) != Bc.out.view(torch.int16)).float().mean().item())
-    del comb_p
+    del comb_p, out_p
 
     # Cold-cache phase times (secondary): before each phase call, 1 GiB of
     # scratch is written so that nothing of the previous phase's output (nor
@@ -452,13 +469,13 @@ def main():
             cold[i, p] = e0.elapsed_time(e1)
     del scratch
 
-    note("fastest layer")
     # The fastest composition of one layer on one GPU: the faster dispatch --
     # the direct one, or the send (single launch with early rows where it
     # applies, else the multi-launch call) plus the unpack -- then the
     # pulling combine, timed as whole steps.
     fast = None
     if Tc == T:
+        note(f"{cfg.name}: fastest layer")
         two_call_ms = (early_ms if single is not None else per_phase_ms[0]) + per_phase_ms[1]
         direct_f = moe.moe_dispatch_direct
         if direct_ll is not None and direct_ll[0] < direct_ms:
@@ -509,26 +526,28 @@ def main():
         if Bf is not B:
             flags_f = moe.moe_status(Bf.ws)
             if flags_f:
-                raise SystemExit(f"device error flags {flags_f:#x} in the fastest-path steps")
+                raise SystemExit(f"device error flags {flags_f:#x} in the fastest-path steps ({cfg.name})")
             del Bf, yf
         del out_f
 
     flags = moe.moe_status(B.ws) | moe.moe_status(Bc.ws)
     if flags:
-        raise SystemExit(f"device error flags {flags:#x} in the timed steps")
+        raise SystemExit(f"device error flags {flags:#x} in the timed steps ({cfg.name})")
 
-    # Achievable rates of the phases' access patterns, on the phases' own
-    # buffers (where a buffer lands in memory moves a stream's rate by up to
-    # ~10%): plain streams free of the row lookups and arithmetic.  The pack
-    # reads a bf16 token row and stores k fp8 rows (moe_stream fan-out, tokens
-    # -> recv_q); unpack and combine send are copies (moe_copy, y -> comb, the
-    # dominant phase's bytes); the receive-side sum reads k bf16 rows and
-    # stores one (moe_stream reduction, comb -> out).  They overwrite recv_q,
-    # comb and out, so they run after everything else.
-    note("pattern ceilings")
+    # Ceilings on the phases' own buffers (where a buffer lands in memory moves
+    # a stream's rate by up to ~20%), free of row lookups and arithmetic:
+    #   - the HIP runtime's own device-to-device copy (hipMemcpyAsync, y ->
+    #     comb, the dominant phase's bytes) and fill (hipMemsetAsync on comb,
+    #     write-only), independent of this repository's kernels;
+    #   - libmoe_streams' copy of the same bytes, and its streams with the
+    #     pack's pattern (a bf16 token row read, k fp8 rows stored: tokens ->
+    #     recv_q) and the receive-side sum's (k bf16 rows read, one stored:
+    #     comb -> out).
+    # They overwrite recv_q, comb and out, so they run after everything else.
+    note(f"{cfg.name}: ceilings")
     dom = max(range(4), key=lambda p: per_phase_ms[p])
     copy_bytes = (nbytes[PHASES[dom]] // 2) // 16 * 16
-    assert copy_bytes <= y.numel() * 2 and copy_bytes <= Bc.comb.numel() * 2
+    copy_bytes = min(copy_bytes, y.numel() * 2 // 16 * 16, Bc.comb.numel() * 2 // 16 * 16)
 
     def rate(fn, moved):
         for _ in range(2):
@@ -545,16 +564,21 @@ def main():
     u_red = cfg.N * Tc * cfg.H * 2 // 16       # the bf16 combine output, in 16-B units
     assert 2 * u_fan * 16 == x.numel() * 2 and cfg.k * u_fan * 16 <= B.recv_q.numel()
     assert cfg.k * u_red * 16 == Bc.comb.numel() * 2 and u_red * 16 == Bc.out.numel() * 2
-    copy_gbs = rate(lambda: moe.moe_copy(Bc.comb, y, copy_bytes), 2 * copy_bytes)
-    fan_gbs = rate(lambda: moe.moe_stream(moe.STREAM_FANOUT, cfg.k, B.recv_q, x, u_fan), (2 + cfg.k) * u_fan * 16)
-    red_gbs = rate(lambda: moe.moe_stream(moe.STREAM_REDUCE, cfg.k, Bc.out, Bc.comb, u_red),
-                   (cfg.k + 1) * u_red * 16)
+    vendor_copy = rate(lambda: hip.copy(Bc.comb, y, copy_bytes, stream), 2 * copy_bytes)
+    vendor_fill = rate(lambda: hip.fill(Bc.comb, copy_bytes, stream), copy_bytes)
+    copy_gbs = rate(lambda: S.moe_copy(Bc.comb, y, copy_bytes), 2 * copy_bytes)
+    fan_gbs = rate(lambda: S.moe_stream(S.STREAM_FANOUT, cfg.k, B.recv_q, x, u_fan), (2 + cfg.k) * u_fan * 16)
+    red_gbs = rate(lambda: S.moe_stream(S.STREAM_REDUCE, cfg.k, Bc.out, Bc.comb, u_red), (cfg.k + 1) * u_red * 16)
     ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays",
                                   "GB/s": round(fan_gbs, 1)},
                 "dispatch_recv": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
                 "combine_send": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
                 "combine_recv": {"pattern": f"reduction: {cfg.k} arrays read, one stored",
                                  "GB/s": round(red_gbs, 1)}}
+    vendor = {"copy_GB/s": round(vendor_copy, 1), "fill_GB/s": round(vendor_fill, 1),
+              "bytes": int(copy_bytes),
+              "what": "hipMemcpyAsync device-to-device y -> comb (GB/s counts bytes read + written) and "
+                      "hipMemsetAsync on comb (bytes written), on the phases' own buffers"}
 
     def info(name, t_ms, t90=None, t50=None):
         """Mean time t_ms (the roofline uses the mean launch duration), with
@@ -568,31 +592,22 @@ def main():
             d["p90_us"] = round(t90 * 1e3, 1)
         return d
 
+    rw = phase_read_write(cfg.N, T, cfg.H, cfg.E, cfg.k, Tc)
     med_ms = np.median(ms, axis=0)
     phase_info = {name: info(name, per_phase_ms[p], p90_ms[p], med_ms[p]) for p, name in enumerate(PHASES)}
     for name, d in phase_info.items():
         d["of_pattern_ceiling"] = round(d["GB/s"] / ceilings[name]["GB/s"], 4)
+        d["of_vendor_copy"] = round(d["GB/s"] / vendor_copy, 4)
+        rb, wb = rw[name]
+        d["read_write_bytes"] = [rb, wb]
     if single is not None:
         single["dispatch_send"] = info("dispatch_send", single_ms, single_p90)
         single["early_rows"]["dispatch_send"] = info("dispatch_send", early_ms)
     dom_name = PHASES[dom]
     achieved = nbytes[dom_name] / (per_phase_ms[dom] * 1e-3) / 1e9
-    kernel = kernel_of(dom_name, B.rows if dom_name.startswith("dispatch") else Bc.rows, cfg.N * Tc)
-    value = total / (step_ms * 1e-3) / 1e9
+    kernel = kernel_of(dom_name)
     batch = f"T={T}" if Tc == T else f"dispatch T={T}, combine T={Tc}"
     res = {
-        "metric": "dispatch / combine us per layer and effective HBM GB/s (% of ~8 TB/s peak)",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.note}; packed receive regions", "N": cfg.N, "T": T, "T_comb": Tc,
                    "H": cfg.H, "E": cfg.E, "k": cfg.k, "region_rows": 0, "batch": batch, "seed": cfg.seed,
                    "payload": "bf16 in, e4m3fn+fp32 block-128 scales dispatched, bf16 combined with fp32 accumulation"},
@@ -600,6 +615,7 @@ def main():
         "phases_cold_cache": {name: {"median_us": round(float(np.median(cold[:, p])) * 1e3, 1),
                                      "p90_us": round(float(np.percentile(cold[:, p], 90)) * 1e3, 1)}
                               for p, name in enumerate(PHASES)},
+        "step_us": round(step_ms * 1e3, 1),
         "dispatch_us": round((per_phase_ms[0] + per_phase_ms[1]) * 1e3, 1),
         "combine_us": round((per_phase_ms[2] + per_phase_ms[3]) * 1e3, 1),
         "dispatch_frac": round((nbytes["dispatch_send"] + nbytes["dispatch_recv"]) /
@@ -621,15 +637,117 @@ def main():
         "graph_step_us": round(graph_step_ms * 1e3, 1),
         "single_launch_dispatch": single,
         "fastest_layer": fast,
+        "vendor_ceilings": vendor,
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "pattern_ceilings": ceilings,
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(kernel, cfg.name)},
-        "cpu_baseline": cpu_single,
-        "cpu_baseline_parallel": cpu_par,
     }
-    print(json.dumps(res), flush=True)
+    del B, Bc, x, y, out_pull
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, total, step_ms
+
+
+def summary(r):
+    """The per-workload entry of the JSON line: phase medians and rates, the
+    dispatch / combine fractions, the step, the fastest layer and the
+    ceilings."""
+    return {
+        "config": r["config"]["workload"],
+        "phases": {p: {k: v for k, v in d.items() if k in ("median_us", "us", "GB/s", "frac", "of_vendor_copy",
+                                                               "of_pattern_ceiling")}
+                   for p, d in r["phases"].items()},
+        "dispatch_frac": r["dispatch_frac"], "combine_frac": r["combine_frac"],
+        "dispatch_us": r["dispatch_us"], "combine_us": r["combine_us"],
+        "step_us": r["step_us"], "graph_step_us": r["graph_step_us"],
+        "fastest_layer": r["fastest_layer"],
+        "combine_pull_us": r["combine_pull"]["us"],
+        "dispatch_direct_us": r["dispatch_direct"]["us"],
+        "dispatch_direct_ll_us": (r["dispatch_direct"]["single_launch"] or {}).get("us"),
+        "dispatch_send_ll_us": ((r["single_launch_dispatch"] or {}).get("dispatch_send") or {}).get("us"),
+        "dispatch_send_ll_early_rows_us": (((r["single_launch_dispatch"] or {}).get("early_rows") or {})
+                                           .get("dispatch_send") or {}).get("us"),
+        "combine_partial_us": r["combine_partial"]["us"],
+        "vendor_ceilings": {k: v for k, v in r["vendor_ceilings"].items() if k.endswith("GB/s")},
+        "pattern_ceilings_GB/s": {p: c["GB/s"] for p, c in r["pattern_ceilings"].items()},
+        "roofline_kernel": r["roofline"]["kernel"], "roofline_frac": r["roofline"]["frac"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="combine_heavy", help="the headline workload")
+    ap.add_argument("--workloads", default="all",
+                    help="other workloads measured in the same run: all, none, or a comma-separated list")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: all N logical EP ranks live in one MI355X's HBM, so --gpus {args.gpus} "
+              "is not a configuration of this benchmark (the multi-GPU sharding is a design, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    others = [] if args.workloads == "none" else (
+        [w for w in ALL_WORKLOADS if w != cfg.name] if args.workloads == "all" else
+        [w for w in args.workloads.split(",") if w and w != cfg.name])
+    for w in others:
+        if w not in W.CONFIGS:
+            raise SystemExit(f"unknown workload {w}")
+    # The CPU baselines run first: the parallel one starts processes, which
+    # should happen before this process initialises the GPU.
+    cpu_single = cpu_par = None
+    if not args.no_cpu_baseline:
+        note("cpu baseline: the oracle, one process")
+        cpu_single = cpu_baseline(args.cpu_sample_tokens)
+        procs = min(16, len(os.sched_getaffinity(0)))
+        note(f"cpu baseline: the oracle, {procs} processes")
+        cpu_par = cpu_baseline_parallel(max(1, args.cpu_sample_tokens // 8), procs)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    import combine_lds_atomic_amd  # noqa: F401  (loads the library beside torch's HIP runtime)
+    hip = HipRuntime()
+
+    note(f"gpu: {cfg.name}, {args.warmup} warm-up and {args.steps} timed steps")
+    res, total, step_ms = measure(cfg, args, dev, stream, hip)
+    wl = {}
+    for name in others:
+        note(f"gpu: {name}, {args.warmup} warm-up and {args.steps} timed steps")
+        r, _, _ = measure(W.CONFIGS[name], args, dev, stream, hip)
+        wl[name] = summary(r)
+
+    value = total / (step_ms * 1e-3) / 1e9
+    line = {
+        "metric": "dispatch / combine us per layer and effective HBM GB/s (% of ~8 TB/s peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE,
+        "data": "synthetic",
+        "sources_digest": _kernel_sources_digest(),
+    }
+    line.update(res)
+    line["workloads"] = wl
+    line["cpu_baseline"] = cpu_single
+    line["cpu_baseline_parallel"] = cpu_par
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -85,6 +85,7 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->exp_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.L + 1)));
   W->src_in_exp = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1) * D.E));
   W->local = reinterpret_cast<int*>(take(D.B > 1 ? sizeof(int) * (size_t)D.N * D.TK : 0));
+  W->umap = reinterpret_cast<int2*>(take(sizeof(int2) * (size_t)D.rows));
   // Exchange area of the single-launch dispatch (one routing chunk per rank
   // only), last so that moe_workspace_init clears it with the header.
   const bool ll = D.B == 1;

@@ -4,41 +4,28 @@
 // routing is already known from dispatch, rows go back with one contiguous
 // write per peer and the receive side accumulates them into the output).
 //
-//   k_comb_send          comb[row_src[i]] = y[i] (after a fixed-region
-//                        overflow, also zero rows for the slots left without
-//                        a row): one 1024-thread workgroup per CU copies its
-//                        range of expert-major rows as one flat range of
-//                        16-byte units, thread-interleaved
-//   k_comb_send_rows     the same with one wave per row (problems below
-//                        131072 rows)
-//   k_comb_recv          each workgroup streams a contiguous range of
-//                        tokens: fp32 sum over slots of w * y, bf16 out; one
-//                        1024-thread workgroup per CU, thread-interleaved
-//                        16-byte output units (k_comb_recv_tokens: one wave
-//                        per token, below 16384 tokens)
-//   k_comb_pull          the same sum, rows read in place (expert-major);
-//                        k_comb_pull_tokens below 16384 tokens
-//   k_comb_send_partial  send-side partial sums: one bf16 row per (token,
-//                        destination rank) group ("Evaluation:
-//                        dispatch/combine latency": accumulating on the send
-//                        side cuts the data sent); one 1024-thread
-//                        workgroup per CU on chunks of tokens,
-//                        thread-interleaved 16-byte units
-//                        (k_comb_send_partial_tokens: one wave per token,
-//                        below 16384 tokens)
-//   k_comb_recv_partial  the receive side of it: fp32 sum of a token's group
-//                        rows, bf16 out
+//   k_comb_send_os        comb[row_src[p]] = y[p], one 16-byte unit per
+//                         thread over the valid expert-major rows
+//                         (k_comb_zero_dropped after a fixed-region
+//                         overflow: zero rows for the slots left without a
+//                         row)
+//   k_comb_recv_os        out = bf16(sum_j w_j * y_j), float32 in slot order,
+//                         one 16-byte output unit per thread
+//   k_comb_pull_os        the same sum, rows read in place (expert-major)
+//   k_comb_send_partial   send-side partial sums: one bf16 row per (token,
+//                         destination rank) group ("Evaluation:
+//                         dispatch/combine latency": accumulating on the send
+//                         side cuts the data sent); one 1024-thread
+//                         workgroup per CU on chunks of tokens,
+//                         thread-interleaved 16-byte units
+//                         (k_comb_send_partial_tokens: one wave per token,
+//                         below 16384 tokens)
+//   k_comb_recv_partial_os  the receive side of it: float32 sum of a token's
+//                         group rows, bf16 out
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kRowsPerPass = 8;   // rows whose metadata one wave resolves at once
-constexpr int kCsWaves = kCombSendShape.waves, kCsThreads = kCombSendShape.threads();
-// 16-B loads per lane issued together while copying a row.  A 7168-wide bf16
-// row needs 14; 32 (with 8-wave workgroups, two per CU) measured 2-5% faster
-// than 16 with 16-wave workgroups, in one process at three workloads.
-constexpr int kCsUnroll = 32;
-constexpr int kCrWaves = kCombRecvShape.waves, kCrThreads = kCombRecvShape.threads();
 
 // acc = fl(acc + fl(w * y)) in slot order, never fused into an FMA.
 __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
@@ -52,8 +39,17 @@ __device__ __forceinline__ void acc_row8(float* acc, float w, const v4u& v) {
   }
 }
 
-constexpr int kSlotGroup = 8;
-constexpr int kCombPieces = 2;   // 1 KB pieces read per slot row per step
+// bf16 bits of 8 float32 sums, packed for one 16-byte store.
+__device__ __forceinline__ v4u pack_bf16x8(const float* acc) {
+  v4u o;
+  o[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o[2] = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o[3] = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  return o;
+}
+
+constexpr int kSlotGroup = 8;     // slot rows loaded together per sum step
 
 // Expert-major row of a slot of source s with expert e and sender position
 // sp, found from the routing tables: the row combine_send would copy back.
@@ -105,124 +101,57 @@ __device__ void zero_dropped_rows(const Dims& D, const Ws& W, uint16_t* __restri
   }
 }
 
-__global__ __launch_bounds__(kCsThreads) void k_comb_send_rows(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                           const int* __restrict__ row_src,
-                                                           uint16_t* __restrict__ comb) {
-  __shared__ int svp[kMaxN + 1];
-  __shared__ int sbase[kMaxN + 1];
-  for (int i = threadIdx.x; i <= D.N; i += kCsThreads) {
-    svp[i] = W.vprefix[i];
-    sbase[i] = W.base[i];
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int ncomb = D.N * D.TK;
-  const int n16 = D.H / 8;
-  int lo, hi;
-  block_range(svp[D.N], lo, hi);      // valid rows, in region order
-  // Wave wv takes rows lo + wv, lo + wv + kCsWaves, ...: the workgroup's
-  // waves work on neighbouring rows at any moment.
-  for (int g0 = lo + wv; g0 < hi; g0 += kCsWaves * kRowsPerPass) {
-    int src = -1, dst = -1;
-    const int g = g0 + lane * kCsWaves;
-    if (lane < kRowsPerPass && g < hi) {
-      const int d = floor_index(svp, D.N + 1, g);
-      const int p = sbase[d] + (g - svp[d]);
-      if (p < D.rows) {
-        const int rs = row_src[p];
-        if (rs >= 0 && rs < ncomb) {
-          src = p;
-          dst = rs;
-        }
-      }
-    }
-    for (int r = 0; r < kRowsPerPass; ++r) {
-      const int sr = __builtin_amdgcn_readlane(src, r);
-      const int dr = __builtin_amdgcn_readlane(dst, r);
-      if (sr < 0) continue;
-      wave_copy16<kCsUnroll>(reinterpret_cast<v4u*>(comb + (int64_t)dr * D.H),
-                      reinterpret_cast<const v4u*>(y + (int64_t)sr * D.H), n16, lane);
-    }
-  }
-  if (D.R) zero_dropped_rows<kCsWaves>(D, W, comb);   // packed regions never overflow
-}
+// ------------------------------------------------------------------ one-shot forms
+constexpr int kOsMaxTileRows = kOsThreads / 16 + 2;     // rows a tile spans (at least 16 units per row)
 
-// The same copy with the whole workgroup on consecutive rows: the
-// workgroup's range of valid rows is one flat range of 16-byte units, and
-// thread t copies units t, t + kCcThreads, ... (kCcUnroll per step, loads
-// before stores), each to its row's comb position.  This is the access
-// pattern of the plain copy; a copy probe with one wave per row ran 4%
-// slower than it on the same data.  Measured in one process, alternating
-// calls: 5% faster than k_comb_send_rows from combine-heavy size up (prefill 6%,
-// Kimi 4%), 7% slower at the decode shape; hence the switch by row count.
-// Each unit's load waits for its row_src: issuing the loads first, with
-// the row_src reads beside them, made this form 5% slower than the per-row
-// one at combine-heavy size.
-constexpr int kCcThreads = 1024, kCcUnroll = 16;
-__global__ __launch_bounds__(kCcThreads) void k_comb_send(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                               const int* __restrict__ row_src,
-                                                               uint16_t* __restrict__ comb) {
-  __shared__ int svp[kMaxN + 1];
-  __shared__ int sbase[kMaxN + 1];
-  for (int i = threadIdx.x; i <= D.N; i += kCcThreads) {
-    svp[i] = W.vprefix[i];
-    sbase[i] = W.base[i];
-  }
-  __syncthreads();
-  const int ncomb = D.N * D.TK;
+// Combine send, one-shot: comb[row_src[p]] = y[p] over the valid rows
+// (region order), one 16-byte unit per thread.  The tile's rows are resolved
+// into LDS first (physical row, and its comb row from row_src).
+__global__ __launch_bounds__(kOsThreads) void k_comb_send_os(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                            const int* __restrict__ row_src,
+                                                            uint16_t* __restrict__ comb) {
+  __shared__ int t_src[kOsMaxTileRows], t_dst[kOsMaxTileRows];
   const int n16 = D.H / 8;
-  int lo, hi;
-  block_range(svp[D.N], lo, hi);      // valid rows, in region order
+  const int valid = W.vprefix[D.N];
+  const int64_t units = (int64_t)valid * n16;
+  const int ncomb = D.N * D.TK;
   const v4u* __restrict__ ys = reinterpret_cast<const v4u*>(y);
   v4u* __restrict__ cs = reinterpret_cast<v4u*>(comb);
-  // This thread's unit (valid row g, column c), advanced by kCcThreads units
-  // per slot and kCcUnroll * kCcThreads per step without dividing again.
-  const int dg1 = kCcThreads / n16, dc1 = kCcThreads % n16;
-  const int64_t first = (int64_t)lo * n16 + threadIdx.x;
-  int g = (int)(first / n16), c = (int)(first - (int64_t)g * n16);
-  while (g < hi) {
-    v4u v[kCcUnroll];
-    int dst[kCcUnroll];
-    int gu = g, cu = c;
-#pragma unroll
-    for (int u = 0; u < kCcUnroll; ++u) {
-      dst[u] = -1;
-      if (gu < hi) {
-        const int d = floor_index(svp, D.N + 1, gu);
-        const int p = sbase[d] + (gu - svp[d]);
-        if (p < D.rows) {
-          const int rs = row_src[p];
-          if (rs >= 0 && rs < ncomb) {
-            dst[u] = rs;
-            v[u] = ld16(ys + (int64_t)p * n16 + cu);
-          }
-        }
+  for (int64_t tile = blockIdx.x; tile * kOsThreads < units; tile += gridDim.x) {
+    const int64_t u0 = tile * kOsThreads;
+    int g0, g, c;
+    os_tile_pos(u0, n16, g0, g, c);
+    const int64_t ul = u0 + kOsThreads - 1 < units ? u0 + kOsThreads - 1 : units - 1;
+    const int nr = (int)(ul - (int64_t)g0 * n16) / n16 + 1;
+    __syncthreads();   // the previous tile's reads of the table are done
+    for (int i = threadIdx.x; i < nr; i += kOsThreads) {
+      const int gi = g0 + i;
+      int p = gi;                                  // packed regions: valid row gi is physical row gi
+      if (D.R) {
+        const int d = floor_index(W.vprefix, D.N + 1, gi);
+        p = W.base[d] + (gi - W.vprefix[d]);
       }
-      gu += dg1;
-      cu += dc1;
-      if (cu >= n16) {
-        cu -= n16;
-        ++gu;
+      int dst = -1;
+      if (p < D.rows) {
+        const int rs = row_src[p];
+        if (rs >= 0 && rs < ncomb) dst = rs;
       }
+      t_src[i] = dst >= 0 ? p : -1;
+      t_dst[i] = dst;
     }
-    gu = g;
-    cu = c;
-#pragma unroll
-    for (int u = 0; u < kCcUnroll; ++u) {
-      if (dst[u] >= 0) st16(cs + (int64_t)dst[u] * n16 + cu, v[u]);
-      gu += dg1;
-      cu += dc1;
-      if (cu >= n16) {
-        cu -= n16;
-        ++gu;
-      }
+    __syncthreads();
+    if (u0 + threadIdx.x < units) {
+      const int r = g - g0;
+      if (t_src[r] >= 0) st16(cs + (int64_t)t_dst[r] * n16 + c, ld16(ys + (int64_t)t_src[r] * n16 + c));
     }
-    g = gu;
-    c = cu;
   }
-  if (D.R) zero_dropped_rows<kCcThreads / kWave>(D, W, comb);   // packed regions never overflow
 }
 
+// After a fixed-region overflow: the zero rows of valid slots left without a
+// row (see zero_dropped_rows), as a kernel of its own beside the one-shot send.
+__global__ __launch_bounds__(1024) void k_comb_zero_dropped(Dims D, Ws W, uint16_t* __restrict__ comb) {
+  zero_dropped_rows<16>(D, W, comb);
+}
 
 // Per lane j < k: whether slot j leads its group, i.e. has a row (dest >= 0)
 // and no earlier slot of the token has a row on the same rank.
@@ -237,166 +166,95 @@ __device__ __forceinline__ bool group_leader(int dest, int k, int lane) {
 
 enum class CombMode { kRecv, kPull, kRecvPartial };
 
-// The weighted sum of one combine, token by token.
-//   kRecv: slot rows are rank s's returned rows comb[s*T*k + send_pos];
-//   kPull: they are read where the expert wrote them, y_em[base[d] +
-//          expert-major index], found from the routing tables;
-//   kRecvPartial: only group leaders contribute, with weight 1, their rows
-//          comb[s*T*k + send_pos] holding the group's partial sum.
-template <CombMode MODE>
-__device__ __forceinline__ void combine_tokens(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
-                                               const int* __restrict__ idx, const int* __restrict__ send_pos,
-                                               const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  int lo, hi;
-  block_range(D.N * D.T, lo, hi);
-  for (int tok = lo + wv; tok < hi; tok += kCrWaves) {
-    const int s = tok / D.T;
-    int row = -1;
-    float wt = 0.0f;
-    if (MODE == CombMode::kRecvPartial) {
-      int dest = -1, sp = -1;
-      if (lane < D.k) {
-        sp = send_pos[(int64_t)tok * D.k + lane];
-        const int e = idx[(int64_t)tok * D.k + lane];
-        if (em_row_of(D, W, s, e, sp) >= 0) dest = e / D.L;
-      }
-      if (group_leader(dest, D.k, lane) && lane < D.k) row = s * D.TK + sp;
-      wt = 1.0f;
-    } else if (lane < D.k) {
-      const int sp = send_pos[(int64_t)tok * D.k + lane];
-      wt = topk_w[(int64_t)tok * D.k + lane];
-      if (MODE == CombMode::kRecv) {
-        if (sp >= 0 && sp < D.TK) row = s * D.TK + sp;
-      } else {
-        row = em_row_of(D, W, s, idx[(int64_t)tok * D.k + lane], sp);
-      }
-    }
-    uint16_t* orow = out + (int64_t)tok * D.H;
-    // Each step reads kCombPieces adjacent 1 KB pieces of every slot row
-    // (kCombPieces KB contiguous per row), lane l holding elements
-    // [base + c*512 + 8l, +8) of piece c.
-    for (int base = 0; base < D.H; base += kWave * 8 * kCombPieces) {
-      float acc[kCombPieces][8];
-#pragma unroll
-      for (int c = 0; c < kCombPieces; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
-      for (int j0 = 0; j0 < D.k; j0 += kSlotGroup) {
-        v4u v[kSlotGroup][kCombPieces];
-        int rr[kSlotGroup];
-#pragma unroll
-        for (int jj = 0; jj < kSlotGroup; ++jj) {
-          const int j = j0 + jj;
-          rr[jj] = j < D.k ? __builtin_amdgcn_readlane(row, j) : -1;
-#pragma unroll
-          for (int c = 0; c < kCombPieces; ++c) {
-            const int col = base + c * kWave * 8 + lane * 8;
-            v[jj][c] = rr[jj] >= 0 && col < D.H
-                           ? ld16(reinterpret_cast<const v4u*>(rows + (int64_t)rr[jj] * D.H + col))
-                           : v4u{0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < kSlotGroup; ++jj) {
-          const int j = j0 + jj;
-          const float wj =
-              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), j < D.k ? j : 0));
-          if (rr[jj] >= 0) {
-#pragma unroll
-            for (int c = 0; c < kCombPieces; ++c) acc_row8(acc[c], wj, v[jj][c]);
-          }
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < kCombPieces; ++c) {
-        const int col = base + c * kWave * 8 + lane * 8;
-        if (col >= D.H) continue;
-        v4u o;
-        o[0] = f32_to_bf16_rne(acc[c][0]) | (f32_to_bf16_rne(acc[c][1]) << 16);
-        o[1] = f32_to_bf16_rne(acc[c][2]) | (f32_to_bf16_rne(acc[c][3]) << 16);
-        o[2] = f32_to_bf16_rne(acc[c][4]) | (f32_to_bf16_rne(acc[c][5]) << 16);
-        o[3] = f32_to_bf16_rne(acc[c][6]) | (f32_to_bf16_rne(acc[c][7]) << 16);
-        st16(reinterpret_cast<v4u*>(orow + col), o);
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(kCrThreads) void k_comb_recv_tokens(Dims D, Ws W, const uint16_t* __restrict__ comb,
-                                                           const int* __restrict__ send_pos,
-                                                           const float* __restrict__ topk_w,
-                                                           uint16_t* __restrict__ out) {
-  combine_tokens<CombMode::kRecv>(D, W, comb, nullptr, send_pos, topk_w, out);
-}
-
-__global__ __launch_bounds__(kCrThreads) void k_comb_pull_tokens(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                           const int* __restrict__ idx,
-                                                           const int* __restrict__ send_pos,
-                                                           const float* __restrict__ topk_w,
-                                                           uint16_t* __restrict__ out) {
-  combine_tokens<CombMode::kPull>(D, W, y, idx, send_pos, topk_w, out);
-}
-
-__global__ __launch_bounds__(kCrThreads) void k_comb_recv_partial(Dims D, Ws W, const uint16_t* __restrict__ comb,
-                                                                   const int* __restrict__ idx,
-                                                                   const int* __restrict__ send_pos,
-                                                                   uint16_t* __restrict__ out) {
-  combine_tokens<CombMode::kRecvPartial>(D, W, comb, idx, send_pos, nullptr, out);
-}
-
-// bf16 bits of 8 float32 sums, packed for one 16-byte store.
-__device__ __forceinline__ v4u pack_bf16x8(const float* acc) {
-  v4u o;
-  o[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  o[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-  o[2] = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-  o[3] = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-  return o;
-}
-
-// The receive-side sums with the whole workgroup on a chunk of consecutive
-// tokens (the plain copy's pattern, as k_comb_send): the chunk's slot rows
-// and weights are resolved into LDS, then thread t forms the output's
-// 16-byte units t, t + kCoThreads, ..., each from the same 16 bytes of the
-// token's k slot rows, summed in slot order exactly as combine_tokens does.
-// Measured in one process, alternating calls: 1.5-2% faster than the
-// one-wave-per-token form from combine-heavy size up (1655-1661 against
-// 1683-1691 us; prefill 3300-3318 against 3360-3391), equal at the decode
-// shape, 50% slower at the tiny one; hence the switch by token count.
-// One or two workgroups per CU and 4, 8 or 16 units per thread were within
-// 1% of each other.
-constexpr int kCoThreads = 1024, kCoUnits = 8, kCoTable = 4096;
-template <CombMode MODE>
-__device__ __forceinline__ void combine_tokens_coop(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
-                                                    const int* __restrict__ idx, const int* __restrict__ send_pos,
-                                                    const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
-  __shared__ int t_row[kCoTable];
-  __shared__ float t_w[kCoTable];
+// The weighted sums, one-shot: one 16-byte output unit (8 elements of a
+// token row) per thread.  The tile's tokens have their slots resolved into
+// LDS first (slot row, weight; for kRecvPartial only group leaders keep a
+// row, with weight 1), then every thread loads the same 16 bytes of each of
+// its token's slot rows and sums them in slot order (acc = fl(acc +
+// fl(w * y)), no fused multiply-add).
+// U output units per thread (tiles of U * kOsThreads units): 1 for the plain
+// and pulling sums; 2 for the sum of group rows, whose slot resolution (the
+// routing-table lookups and the leader pass) costs more per tile and is
+// amortised over twice the units (5-12% faster than 1 from the tiny to the
+// prefill shape; 4 was slower).  For the other two, 2 and 4 were 2-15% slower.
+template <int U>
+constexpr int os_tile_tokens() { return kOsThreads * U / 16 + 2; }   // tokens a tile spans (>= 16 units per row)
+template <CombMode MODE, int U>
+__device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
+                                           const int* __restrict__ idx, const int* __restrict__ send_pos,
+                                           const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
+  constexpr int kTile = kOsThreads * U;
+  constexpr int kOsSlotTable = os_tile_tokens<U>() * kMaxK;
+  __shared__ int t_row[kOsSlotTable];
+  __shared__ float t_w[kOsSlotTable];
+  __shared__ int t_dest[MODE == CombMode::kRecvPartial ? kOsSlotTable : 1];
   const int n16 = D.H / 8, k = D.k;
-  int ntok = kCoThreads * kCoUnits / n16;                 // tokens per chunk
-  ntok = max(1, min(ntok, kCoTable / k));
+  const int64_t units = (int64_t)D.N * D.T * n16;
   const v4u* __restrict__ rs = reinterpret_cast<const v4u*>(rows);
   v4u* __restrict__ os = reinterpret_cast<v4u*>(out);
-  int lo, hi;
-  block_range(D.N * D.T, lo, hi);
-  for (int t0 = lo; t0 < hi; t0 += ntok) {
-    const int nt = min(ntok, hi - t0);
-    for (int i = threadIdx.x; i < nt * k; i += kCoThreads) {
+  for (int64_t tile = blockIdx.x; tile * kTile < units; tile += gridDim.x) {
+    const int64_t u0 = tile * kTile;
+    int t0, tok, c;
+    os_tile_pos(u0, n16, t0, tok, c);
+    const int64_t ul = u0 + kTile - 1 < units ? u0 + kTile - 1 : units - 1;
+    const int nt = (int)(ul - (int64_t)t0 * n16) / n16 + 1;
+    __syncthreads();   // the previous tile's reads of the tables are done
+    for (int i = threadIdx.x; i < nt * k; i += kOsThreads) {
       const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
       const int s = (t0 + i / k) / D.T;
       const int sp = send_pos[slot];
       int row;
-      if (MODE == CombMode::kRecv) row = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
-      else row = em_row_of(D, W, s, idx[slot], sp);
+      if constexpr (MODE == CombMode::kRecv) {
+        row = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
+      } else {
+        const int e = idx[slot];
+        row = em_row_of(D, W, s, e, sp);
+        if constexpr (MODE == CombMode::kRecvPartial) {
+          t_dest[i] = row >= 0 ? e / D.L : -1;
+          row = row >= 0 ? s * D.TK + sp : -1;
+        }
+      }
       t_row[i] = row;
-      t_w[i] = topk_w[slot];
+      if constexpr (MODE == CombMode::kRecvPartial) t_w[i] = 1.0f;
+      else t_w[i] = topk_w[slot];
+    }
+    if constexpr (MODE == CombMode::kRecvPartial) {
+      // A slot with a row leads its group unless an earlier slot of the
+      // token has a row on the same rank; only leaders' group rows are summed.
+      __syncthreads();
+      constexpr int kQ = kOsSlotTable / kOsThreads + 1;
+      bool lead[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int i = threadIdx.x + q * kOsThreads;
+        lead[q] = false;
+        if (i < nt * k) {
+          const int j = i % k, b = i - j, d = t_dest[i];
+          bool l = d >= 0;
+          for (int jj = 0; jj < j; ++jj) l = l && t_dest[b + jj] != d;
+          lead[q] = l;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int i = threadIdx.x + q * kOsThreads;
+        if (i < nt * k && !lead[q]) t_row[i] = -1;
+      }
     }
     __syncthreads();
-    for (int f = threadIdx.x; f < nt * n16; f += kCoThreads) {
-      const int tt = f / n16, c = f - tt * n16;
-      const int* tr = t_row + tt * k;
-      const float* tw = t_w + tt * k;
+    for (int q = 0; q < U; ++q) {
+      const int64_t uu = u0 + threadIdx.x + q * kOsThreads;
+      if (q > 0) {   // this thread's next unit, kOsThreads further on
+        c += kOsThreads;
+        while (c >= n16) {
+          c -= n16;
+          ++tok;
+        }
+      }
+      if (uu >= units) break;
+      const int* tr = t_row + (tok - t0) * k;
+      const float* tw = t_w + (tok - t0) * k;
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -412,25 +270,31 @@ __device__ __forceinline__ void combine_tokens_coop(const Dims& D, const Ws& W, 
         for (int jj = 0; jj < kSlotGroup; ++jj)
           if (rr[jj] >= 0) acc_row8(acc, tw[j0 + jj], v[jj]);
       }
-      st16(os + (int64_t)(t0 + tt) * n16 + c, pack_bf16x8(acc));
+      st16(os + uu, pack_bf16x8(acc));
     }
-    __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(kCoThreads) void k_comb_recv(Dims D, Ws W, const uint16_t* __restrict__ comb,
-                                                               const int* __restrict__ send_pos,
-                                                               const float* __restrict__ topk_w,
-                                                               uint16_t* __restrict__ out) {
-  combine_tokens_coop<CombMode::kRecv>(D, W, comb, nullptr, send_pos, topk_w, out);
+__global__ __launch_bounds__(kOsThreads) void k_comb_recv_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
+                                                            const int* __restrict__ send_pos,
+                                                            const float* __restrict__ topk_w,
+                                                            uint16_t* __restrict__ out) {
+  combine_os<CombMode::kRecv, 1>(D, W, comb, nullptr, send_pos, topk_w, out);
 }
 
-__global__ __launch_bounds__(kCoThreads) void k_comb_pull(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                               const int* __restrict__ idx,
-                                                               const int* __restrict__ send_pos,
-                                                               const float* __restrict__ topk_w,
-                                                               uint16_t* __restrict__ out) {
-  combine_tokens_coop<CombMode::kPull>(D, W, y, idx, send_pos, topk_w, out);
+__global__ __launch_bounds__(kOsThreads) void k_comb_pull_os(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                            const int* __restrict__ idx,
+                                                            const int* __restrict__ send_pos,
+                                                            const float* __restrict__ topk_w,
+                                                            uint16_t* __restrict__ out) {
+  combine_os<CombMode::kPull, 1>(D, W, y, idx, send_pos, topk_w, out);
+}
+
+__global__ __launch_bounds__(kOsThreads) void k_comb_recv_partial_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
+                                                                    const int* __restrict__ idx,
+                                                                    const int* __restrict__ send_pos,
+                                                                    uint16_t* __restrict__ out) {
+  combine_os<CombMode::kRecvPartial, 2>(D, W, comb, idx, send_pos, nullptr, out);
 }
 
 // Send-side partial sums, token by token (one wave per token; the form for
@@ -651,45 +515,27 @@ __global__ __launch_bounds__(kPsThreads) void k_comb_send_partial(Dims D, Ws W, 
   }
 }
 
-constexpr int64_t kCcMinRows = 131072;   // rows from which the cooperative form is used
-
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
-  if ((int64_t)D.rows >= kCcMinRows) {
-    const int64_t need = ((int64_t)D.rows * (D.H / 8) + kCcThreads * kCcUnroll - 1) / (kCcThreads * kCcUnroll);
-    const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
-    return launch("k_comb_send", k_comb_send, dim3(grid), dim3(kCcThreads), 0, st, D, W, y, row_src, comb);
-  }
-  const int grid = stream_grid(kCombSendShape, cus, (int64_t)D.rows, kCsWaves);
-  return launch("k_comb_send_rows", k_comb_send_rows, dim3(grid), dim3(kCsThreads), 0, st, D, W, y, row_src, comb);
-}
-
-constexpr int64_t kCoMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
-static int coop_grid(const Dims& D, int cus) {
-  const int64_t need = ((int64_t)D.N * D.T * (D.H / 8) + kCoThreads * kCoUnits - 1) / (kCoThreads * kCoUnits);
-  const int64_t cap = cus;   // one workgroup per CU
-  return (int)(need < cap ? (need < 1 ? 1 : need) : cap);
+  const int rc = launch("k_comb_send_os", k_comb_send_os, dim3(os_grid((int64_t)D.rows * (D.H / 8))),
+                        dim3(kOsThreads), 0, st, D, W, y, row_src, comb);
+  if (rc != MOE_OK || D.R == 0) return rc;   // packed regions never overflow
+  return launch("k_comb_zero_dropped", k_comb_zero_dropped, dim3(cus), dim3(1024), 0, st, D, W, comb);
 }
 
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  if ((int64_t)D.N * D.T >= kCoMinTokens)
-    return launch("k_comb_recv", k_comb_recv, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, Ws{}, comb,
-                  send_pos, w, out);
-  const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_recv_tokens", k_comb_recv_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, Ws{}, comb, send_pos, w, out);
+  return launch("k_comb_recv_os", k_comb_recv_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8))), dim3(kOsThreads),
+                0, st, D, Ws{}, comb, send_pos, w, out);
 }
 
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  if ((int64_t)D.N * D.T >= kCoMinTokens)
-    return launch("k_comb_pull", k_comb_pull, dim3(coop_grid(D, cus)), dim3(kCoThreads), 0, st, D, W, y, idx,
-                  send_pos, w, out);
-  const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_pull_tokens", k_comb_pull_tokens, dim3(grid), dim3(kCrThreads), 0, st, D, W, y, idx, send_pos, w, out);
+  return launch("k_comb_pull_os", k_comb_pull_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8))), dim3(kOsThreads),
+                0, st, D, W, y, idx, send_pos, w, out);
 }
 
 constexpr int64_t kPsMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
@@ -711,9 +557,8 @@ int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, cons
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
                              uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  const int grid = stream_grid(kCombRecvShape, cus, (int64_t)D.N * D.T, kCrWaves);
-  return launch("k_comb_recv_partial", k_comb_recv_partial, dim3(grid), dim3(kCrThreads), 0, st, D, W, comb, idx,
-                send_pos, out);
+  return launch("k_comb_recv_partial_os", k_comb_recv_partial_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kOsThreads)),
+                dim3(kOsThreads), 0, st, D, W, comb, idx, send_pos, out);
 }
 
 }  // namespace moe

@@ -2,21 +2,24 @@
 // sections "Send and receive buffers", "Dispatch and combine", and
 // "Evaluation: dispatch/combine latency" for the block-scaled fp8 payload).
 //
-//   k_pack    each workgroup streams a contiguous range of tokens, one wave
-//             per token (or per slice of a token when tokens are too few to
-//             fill the GPU): final slot positions, block-128 amax with DPP,
-//             fp8 quantisation, and k 16-byte row stores straight into the
-//             destination ranks' receive regions (the "remote write").
-//   k_unpack  each workgroup streams a contiguous range of expert-major rows:
-//             the receive side finds each row's (expert, source) segment from
-//             the exchanged counts alone and copies it out of the
-//             source-major receive region; one 1024-thread workgroup per CU,
-//             its rows copied as one thread-interleaved range of 16-byte
-//             units.
-//   k_pack_direct  k_pack storing each row at its expert-major row instead
-//             (peers mapped into each other's memory push straight into the
-//             grouped-GEMM layout; on one GPU every rank is such a peer), so
-//             neither the receive regions nor k_unpack are needed.
+//   k_pack_os       one 1024-element pass of one token per wave, workgroups
+//                   in (token, pass) order: final slot positions, block-128
+//                   amax with DPP, fp8 quantisation, and k 16-byte row
+//                   stores straight into the destination ranks' receive
+//                   regions (the "remote write"), with the block scales
+//   k_unpack_index  one thread per expert-major row: the (expert, source)
+//                   segment it belongs to, found from the exchanged counts
+//                   alone; writes row_src and the row map
+//   k_unpack_os     one 16-byte unit per thread: each expert-major row's fp8
+//                   payload, then its scales, copied out of the
+//                   source-major receive region
+//   k_pack_direct_os  k_pack_os storing each row at its expert-major row
+//                   instead (peers mapped into each other's memory push
+//                   straight into the grouped-GEMM layout; on one GPU every
+//                   rank is such a peer), so neither the receive regions
+//                   nor the unpack are needed
+//   k_dispatch_ll, k_dispatch_ll_direct  the send half (or the direct
+//                   dispatch) in one launch, for decode-sized batches
 #include <map>
 #include <tuple>
 #include <mutex>
@@ -151,7 +154,7 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
 
 // The row slot i (of rank s's T*k) is packed to, -1 for none.  DIRECT =
 // false: its source-major receive row; DIRECT = true: its expert-major row,
-// by the same index and rule k_unpack uses (it exists if both it and its
+// by the same index and rule the unpack uses (it exists if both it and its
 // source-major row fit; row_src -1 when only the source-major one does not).
 // With several routing chunks per rank the count kernel left the rank
 // inside the chunk, and the chunk's base for the expert completes it; then
@@ -187,53 +190,6 @@ __device__ __forceinline__ int pack_slot_row(const Dims& D, const Ws& W, const i
     return fits ? pe : -1;
   }
   return -1;
-}
-
-// The pack loop.  DIRECT = false: rows go to the source-major receive
-// regions (recv_q, recv_s).  DIRECT = true: they go straight to their
-// expert-major rows (x_q, x_s), and the loop also writes row_src and
-// exp_off, the outputs of the receive half, which then has nothing left to
-// do.
-template <bool DIRECT>
-__device__ __forceinline__ void pack_tokens(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
-                                            const int* __restrict__ idx, int* __restrict__ send_pos,
-                                            uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
-                                            int* __restrict__ row_src, int* __restrict__ exp_off) {
-  __shared__ float sscale[kPkWaves][kMaxNB];
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kPkThreads) exp_off[i] = W.exp_off[i];
-  int lo, hi;
-  block_range(D.N * D.T * D.slices, lo, hi);
-  for (int item = lo + wv; item < hi; item += kPkWaves) {
-    int tok, sl, h0, h1;
-    item_cols(D, item, tok, sl, h0, h1);
-    const int s = tok / D.T, t = tok - s * D.T;
-    // The item's first token loads go out before its rows are resolved, so
-    // the two latencies overlap: 2-3 us less at the decode shape, no change
-    // from combine-heavy size up (98 VGPRs, 4 workgroups per CU there,
-    // against 65 and 7 without).  Staging the routing tables in LDS as the
-    // unpack does changed nothing here.
-    v4u a[kPackPasses], b[kPackPasses];
-    if (x != nullptr) load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
-    // Lane j < k resolves slot j.
-    const int row = lane < D.k ? pack_slot_row<DIRECT>(D, W, idx, send_pos, row_src, s, t * D.k + lane, sl == 0) : -1;
-    if (x == nullptr) continue;
-    pack_item<true>(D, item, row, x, recv_q, recv_s, sscale[wv], a, b);
-  }
-}
-
-__global__ __launch_bounds__(kPkThreads) void k_pack(Dims D, Ws W, const uint16_t* __restrict__ x,
-                                                     const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                     uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
-  pack_tokens<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
-}
-
-__global__ __launch_bounds__(kPkThreads) void k_pack_direct(Dims D, Ws W, const uint16_t* __restrict__ x,
-                                                            const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                            uint8_t* __restrict__ x_q, float* __restrict__ x_s,
-                                                            int* __restrict__ row_src, int* __restrict__ exp_off) {
-  pack_tokens<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
 }
 
 // ------------------------------------------------------------------ single launch
@@ -673,7 +629,7 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
         if (DIRECT && e >= 0 && e < D.E) {
           // The column workgroup's values: the expert-major row offset and,
           // with fixed regions, the limit below which the source-major row
-          // fits (the rule of k_unpack: the row exists if it fits region d,
+          // fits (the unpack's rule: the row exists if it fits region d,
           // its payload only if the source-major row fits too).
           const int d = e / D.L;
           int sp = 0, off = 0, lim = 0;
@@ -854,93 +810,151 @@ __device__ __forceinline__ void unpack_row(const Dims& D, const Ws& W, const Unp
   }
 }
 
-// The unpack, with the whole workgroup on consecutive rows (the access
-// pattern of the plain copy, as k_comb_send): per chunk of rows, their
-// sources are resolved into LDS, then thread t copies the chunk's 16-byte
-// payload units t, t + kUcThreads, ... (kUcUnroll per step, loads before
-// stores) and its scale units likewise.  Measured in one process,
-// alternating calls, against a form with one wave per row: combine-heavy
-// 1307-1402 against 1403-1461 us, prefill 2633-2697 against 2776-2840, equal
-// at the decode shape, tiny 21 against 25 us, Kimi dispatch 199-201 against
-// 205-213.  (Sixteen units per thread would spill at this workgroup size.)
-constexpr int kUcThreads = 1024, kUcUnroll = 8;
-constexpr int kUcMaxRows = kUcThreads * kUcUnroll / (kScaleBlock / 16);   // rows per chunk at H = 128
-__global__ __launch_bounds__(kUcThreads) void k_unpack(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
-                                                            const float* __restrict__ recv_s,
-                                                            uint8_t* __restrict__ x_q, float* __restrict__ x_s,
-                                                            int* __restrict__ exp_off, int* __restrict__ row_src) {
+// ------------------------------------------------------------------ one-shot unpack
+//
+// The receive half in the one-shot form (kOsThreads threads per workgroup,
+// one 16-byte unit per thread, workgroups in row order): first
+// k_unpack_index maps every valid expert-major row g (region order) to the
+// source-major row it copies -- the segment search of unpack_row, with the
+// workgroup's region tables staged in LDS -- writing row_src and the pair
+// {source row, physical row} into the workspace's umap; then k_unpack_os
+// copies the fp8 payload units of all rows, then (a tile range of its own)
+// their scale units: with each row's 14 scale units interleaved after its
+// 448 payload units (H = 7168) the copy took 1456 us at combine-heavy size,
+// with the two ranges apart 1271 us (the old one-chunk-per-workgroup form:
+// 1411 us).
+__global__ __launch_bounds__(kOsThreads) void k_unpack_index(Dims D, Ws W, int* __restrict__ exp_off,
+                                                             int* __restrict__ row_src) {
   __shared__ int svp[kMaxN + 1];
   __shared__ int stage[kStageInts];
-  __shared__ int t_src[kUcMaxRows], t_dst[kUcMaxRows];
-  for (int i = threadIdx.x; i <= D.N; i += kUcThreads) svp[i] = W.vprefix[i];
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kUcThreads) exp_off[i] = W.exp_off[i];
+  for (int i = threadIdx.x; i <= D.N; i += kOsThreads) svp[i] = W.vprefix[i];
+  if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kOsThreads) exp_off[i] = W.exp_off[i];
   __syncthreads();
-  int lo, hi;
-  block_range(svp[D.N], lo, hi);
-  const UnpackStage S = unpack_stage<kUcThreads>(D, W, svp, stage, lo, hi);
-  const int n16 = D.H / 16;                                    // payload units per row
-  const int rchunk = kUcThreads * kUcUnroll / n16;             // whole rows per chunk (n16 >= 8)
-  const int dr1 = kUcThreads / n16, dc1 = kUcThreads % n16;   // per-slot advance of (row, column)
-  const int r0 = threadIdx.x / n16, c0 = threadIdx.x % n16;
+  const int valid = svp[D.N];
+  for (int64_t lo64 = (int64_t)blockIdx.x * kOsThreads; lo64 < valid; lo64 += (int64_t)gridDim.x * kOsThreads) {
+    const int lo = (int)lo64, hi = min(valid, lo + kOsThreads);
+    const UnpackStage S = unpack_stage<kOsThreads>(D, W, svp, stage, lo, hi);
+    const int g = lo + (int)threadIdx.x;
+    if (g < hi) {
+      int src, dst;
+      unpack_row(D, W, S, svp, g, row_src, src, dst);
+      W.umap[g] = make_int2(dst >= 0 ? src : -1, dst);
+    }
+    __syncthreads();   // the stage is rebuilt for the next range
+  }
+}
+
+__global__ __launch_bounds__(kOsThreads) void k_unpack_os(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
+                                                          const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
+                                                          float* __restrict__ x_s) {
+  const int n16 = D.H / 16;                        // payload units per row
+  const bool s16 = (D.NB & 3) == 0;
+  const int ns = s16 ? D.NB / 4 : D.NB;
+  const int valid = W.vprefix[D.N];
+  const int64_t pay = (int64_t)valid * n16;
+  const int64_t ptiles = (pay + kOsThreads - 1) / kOsThreads;
+  const int64_t sc = (int64_t)valid * ns;
+  const int64_t tiles = ptiles + (sc + kOsThreads - 1) / kOsThreads;
   const v4u* __restrict__ qs = reinterpret_cast<const v4u*>(recv_q);
   v4u* __restrict__ qd = reinterpret_cast<v4u*>(x_q);
-  const bool scales16 = (D.NB & 3) == 0;
-  for (int g0 = lo; g0 < hi; g0 += rchunk) {
-    const int nr = min(rchunk, hi - g0);
-    for (int r = threadIdx.x; r < nr; r += kUcThreads) {
-      int src, dst;
-      unpack_row(D, W, S, svp, g0 + r, row_src, src, dst);
-      t_src[r] = dst >= 0 ? src : -1;
-      t_dst[r] = dst;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    if (tile < ptiles) {
+      const int64_t u0 = tile * kOsThreads;
+      if (u0 + threadIdx.x >= pay) continue;
+      int g0, g, c;
+      os_tile_pos(u0, n16, g0, g, c);
+      const int2 m = W.umap[g];
+      if (m.x >= 0) st16(qd + (int64_t)m.y * n16 + c, ld16(qs + (int64_t)m.x * n16 + c));
+    } else {
+      const int64_t u0 = (tile - ptiles) * kOsThreads;
+      if (u0 + threadIdx.x >= sc) continue;
+      int g0, g, c;
+      os_tile_pos(u0, ns, g0, g, c);
+      const int2 m = W.umap[g];
+      if (m.x < 0) continue;
+      if (s16) st16(reinterpret_cast<v4u*>(x_s + (int64_t)m.y * D.NB) + c, ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)m.x * D.NB) + c));
+      else x_s[(int64_t)m.y * D.NB + c] = recv_s[(int64_t)m.x * D.NB + c];
     }
-    __syncthreads();
-    if (x_q != nullptr) {
-      v4u v[kUcUnroll];
-      int dst[kUcUnroll];
-      int r = r0, c = c0;
-#pragma unroll
-      for (int u = 0; u < kUcUnroll; ++u) {
-        dst[u] = -1;
-        if (r < nr) {
-          const int sr = t_src[r];
-          if (sr >= 0) {
-            dst[u] = t_dst[r];
-            v[u] = ld16(qs + (int64_t)sr * n16 + c);
-          }
-        }
-        r += dr1;
-        c += dc1;
-        if (c >= n16) {
-          c -= n16;
-          ++r;
-        }
-      }
-      c = c0;
-#pragma unroll
-      for (int u = 0; u < kUcUnroll; ++u) {
-        if (dst[u] >= 0) st16(qd + (int64_t)dst[u] * n16 + c, v[u]);
-        c += dc1;
-        if (c >= n16) c -= n16;
-      }
-      // Scales: NB floats per row, as 16-byte units where rows are whole units.
-      if (scales16) {
-        const int s16 = D.NB / 4;
-        for (int f = threadIdx.x; f < nr * s16; f += kUcThreads) {
-          const int rr = f / s16, cc = f - rr * s16;
-          if (t_src[rr] >= 0)
-            st16(reinterpret_cast<v4u*>(x_s + (int64_t)t_dst[rr] * D.NB) + cc,
-                 ld16(reinterpret_cast<const v4u*>(recv_s + (int64_t)t_src[rr] * D.NB) + cc));
-        }
-      } else {
-        for (int f = threadIdx.x; f < nr * D.NB; f += kUcThreads) {
-          const int rr = f / D.NB, cc = f - rr * D.NB;
-          if (t_src[rr] >= 0) x_s[(int64_t)t_dst[rr] * D.NB + cc] = recv_s[(int64_t)t_src[rr] * D.NB + cc];
-        }
-      }
-    }
-    __syncthreads();
   }
+}
+
+// ------------------------------------------------------------------ one-shot pack
+//
+// The pack in the one-shot form: a work item is one pass (1024 elements) of
+// one token, one item per wave, kOsThreads / 64 items per workgroup, items
+// in (token, pass) order, so the workgroups resident at any moment read a
+// window of consecutive tokens and store into the matching runs of every
+// destination's rows.  Each wave resolves its token's k rows itself (lane j,
+// slot j), quantises its 8 blocks of 128 and stores the fp8 bytes and the 8
+// block scales to each of the k rows.  The first pass of a token also writes
+// the slot's position when the count kernel left it (several routing chunks
+// per rank), and in the direct form row_src.
+template <bool DIRECT>
+__device__ __forceinline__ void pack_tokens_os(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
+                                               const int* __restrict__ idx, int* __restrict__ send_pos,
+                                               uint8_t* __restrict__ q_out, float* __restrict__ s_out,
+                                               int* __restrict__ row_src, int* __restrict__ exp_off) {
+  constexpr int kWavesOs = kOsThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kOsThreads) exp_off[i] = W.exp_off[i];
+  const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;   // layout only: one item per token
+  const int64_t items = (int64_t)D.N * D.T * passes;
+  for (int64_t it = (int64_t)blockIdx.x * kWavesOs + wv; it < items; it += (int64_t)gridDim.x * kWavesOs) {
+    const int tok = (int)(it / passes), pass = (int)(it - (int64_t)tok * passes);
+    const int s = tok / D.T, t = tok - s * D.T;
+    const int col = pass * kPackCols + lane * 16;    // this lane's 16 elements
+    const bool act = x != nullptr && col < D.H;
+    v4u a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (act) {
+      const uint16_t* xr = x + (int64_t)tok * D.H + col;
+      a = ld16(reinterpret_cast<const v4u*>(xr));
+      b = ld16(reinterpret_cast<const v4u*>(xr + 8));
+    }
+    // Lane j < k resolves slot j.
+    const int row = lane < D.k ? pack_slot_row<DIRECT>(D, W, idx, send_pos, row_src, s, t * D.k + lane, pass == 0) : -1;
+    if (x == nullptr) continue;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(a[i]);
+      v[2 * i + 1] = bf16_hi(a[i]);
+      v[8 + 2 * i] = bf16_lo(b[i]);
+      v[8 + 2 * i + 1] = bf16_hi(b[i]);
+    }
+    int am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
+    am = max8_lanes(am);                     // amax of the 128-element block
+    const float amax = __uint_as_float((uint32_t)am);
+    const float scale = amax / 448.0f;       // IEEE division, round to nearest even
+    v4u q = {0, 0, 0, 0};
+    if (amax != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
+    }
+    const float sc = amax != 0.0f ? scale : 0.0f;
+    for (int j = 0; j < D.k; ++j) {
+      const int rj = __builtin_amdgcn_readlane(row, j);
+      if (rj < 0 || !act) continue;
+      st16(reinterpret_cast<v4u*>(q_out + (int64_t)rj * D.H + col), q);
+      if ((lane & 7) == 0) s_out[(int64_t)rj * D.NB + col / kScaleBlock] = sc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kOsThreads) void k_pack_os(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                        const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                        uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
+  pack_tokens_os<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
+}
+
+__global__ __launch_bounds__(kOsThreads) void k_pack_direct_os(Dims D, Ws W, const uint16_t* __restrict__ x,
+                                                               const int* __restrict__ idx, int* __restrict__ send_pos,
+                                                               uint8_t* __restrict__ x_q, float* __restrict__ x_s,
+                                                               int* __restrict__ row_src, int* __restrict__ exp_off) {
+  pack_tokens_os<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
 }
 
 // Slices of its hidden dimension each token is split into: doubled while
@@ -956,24 +970,26 @@ static int pack_slices(const Dims& D, int cus, bool payload) {
   return sl;
 }
 
-int launch_pack(const Dims& D0, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
+int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
                 float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st) {
-  if (D0.N * D0.T == 0) return MOE_OK;
-  Dims D = D0;
-  D.slices = pack_slices(D, cus, x != nullptr);
-  const int grid = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
+  if (D.N * D.T == 0) return MOE_OK;
+  const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;
+  const int grid = os_grid((int64_t)D.N * D.T * passes, kOsThreads / kWave);
   if (row_src)
-    return launch("k_pack_direct", k_pack_direct, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out,
-                  s_out, row_src, exp_off);
-  return launch("k_pack", k_pack, dim3(grid), dim3(kPkThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
+    return launch("k_pack_direct_os", k_pack_direct_os, dim3(grid), dim3(kOsThreads), 0, st, D, W, x, idx, send_pos,
+                  q_out, s_out, row_src, exp_off);
+  return launch("k_pack_os", k_pack_os, dim3(grid), dim3(kOsThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
-  const int64_t need = ((int64_t)D.rows * (D.H / 16) + kUcThreads * kUcUnroll - 1) / (kUcThreads * kUcUnroll);
-  const int grid = (int)(need < cus ? (need < 1 ? 1 : need) : cus);
-  return launch("k_unpack", k_unpack, dim3(grid), dim3(kUcThreads), 0, st, D, W, recv_q, recv_s, x_q, x_s, exp_off,
-                row_src);
+  const int rc = launch("k_unpack_index", k_unpack_index, dim3(os_grid(D.rows)), dim3(kOsThreads), 0, st, D, W,
+                        exp_off, row_src);
+  if (rc != MOE_OK || x_q == nullptr || D.rows == 0) return rc;   // layout only
+  const int64_t tiles = ((int64_t)D.rows * (D.H / 16) + kOsThreads - 1) / kOsThreads +
+                        ((int64_t)D.rows * ((D.NB & 3) == 0 ? D.NB / 4 : D.NB) + kOsThreads - 1) / kOsThreads;
+  return launch("k_unpack_os", k_unpack_os, dim3(os_grid(tiles * kOsThreads)), dim3(kOsThreads), 0, st, D, W,
+                recv_q, recv_s, x_q, x_s);
 }
 
 // Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic
@@ -1010,9 +1026,10 @@ int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int
   const void* kernel = direct ? reinterpret_cast<const void*>(k_dispatch_ll_direct)
                               : reinterpret_cast<const void*>(k_dispatch_ll);
   const int layout_wgs = D.N + 1 + (direct ? D.N : 0);
-  // Packers: as many as the k_pack grid would have, but no more than fit on
-  // the GPU beside the layout workgroups, so no packer starts late.  The
-  // direct form needs packers without tokens too (they write row_src).
+  // Packers: one wave per work item (4 per workgroup), at most 8 workgroups
+  // per CU, and no more than fit on the GPU beside the layout workgroups, so
+  // no packer starts late.  The direct form needs packers without tokens too
+  // (they write row_src).
   int npack = 0;
   if (x || direct) {
     const int resident = cus * ll_blocks_per_cu(kernel, lds) - layout_wgs;

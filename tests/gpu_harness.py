@@ -237,3 +237,137 @@ def check_partial_full(r, lay):
             grp = [comb_o[s * T * k + lay.send_pos[s, t, j]] for j in np.flatnonzero(lead[s, t])]
             partial_bound_check(got_out[s, t], rows, np.where(part, r["w"][s, t], 0.0), grp)
     return lead
+
+
+# ------------------------------------------------------------------ full size, every row
+
+def _workers(per_item_bytes: float) -> int:
+    """Host threads for the chunked oracle checks: NumPy releases the GIL in
+    its array loops, so the oracle's per-chunk work runs in parallel; bounded
+    by the cores and by host memory (per_item_bytes each)."""
+    import os
+    try:
+        import psutil
+        avail = psutil.virtual_memory().available
+    except Exception:  # pragma: no cover
+        avail = 32e9
+    budget = min(0.4 * avail, 100e9)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, cores, int(budget // max(per_item_bytes, 1.0))))
+
+
+def _pmap(fn, items, per_item_bytes):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(_workers(per_item_bytes)) as ex:
+        for _ in ex.map(fn, items):
+            pass
+
+
+def _rows(t: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
+    """Rows `rows` of a device array, gathered on the device and brought to
+    the host."""
+    return t[torch.from_numpy(np.ascontiguousarray(rows, np.int64)).to(t.device)].cpu()
+
+
+def check_dispatch_full_size(r, lay: O.Layout, tok_chunk: int = 1024):
+    """Every receive-region row and every expert-major row (fp8 bytes and fp32
+    scales) against the oracle, chunk by chunk: the oracle quantises each
+    chunk of tokens as the check runs (quantize_rows), and each quantised row
+    must sit, bit for bit, at every row dispatch_send / dispatch_recv put it
+    (recv_row, em_row of the oracle's layout)."""
+    sh, B = r["sh"], r["B"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    x = r["x"]
+    items = [(s, t0) for s in range(N) for t0 in range(0, T, tok_chunk)]
+
+    def one(item):
+        s, t0 = item
+        t1 = min(T, t0 + tok_chunk)
+        q, sc = O.quantize_rows(x[s, t0:t1].float().cpu().numpy())
+        for name, rows, gq, gs in (("recv", lay.recv_row, B.recv_q, B.recv_s), ("x", lay.em_row, B.x_q, B.x_s)):
+            rr = rows[s, t0:t1, :]
+            ok = rr >= 0
+            got_q = _rows(gq, rr[ok]).numpy()
+            got_s = _rows(gs, rr[ok]).numpy()
+            tok = np.broadcast_to(np.arange(t1 - t0)[:, None], rr.shape)[ok]
+            assert (got_q == q[tok]).all(), f"{name}_q rank {s} tokens {t0}..{t1}"
+            assert (got_s.view(np.uint32) == sc[tok].view(np.uint32)).all(), f"{name}_s rank {s} tokens {t0}..{t1}"
+
+    _pmap(one, items, tok_chunk * H * (8 + 2 * k * 1.1) + 2 * tok_chunk * H * 8)
+
+
+def check_combine_full_size(r, lay: O.Layout, ranks=None):
+    """Every comb row and every output token of the source ranks `ranks` (all
+    by default) against the oracle, one source rank at a time: the oracle's
+    combine_send places the expert-major rows that return to rank s (those
+    whose row_src falls in s's range), and its combine_recv sums them; comb,
+    out and the pulling combine's output must match (comb bit for bit; out
+    within the combine tolerance, and bit for bit)."""
+    sh, B = r["sh"], r["B"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    rsrc = O.row_src(lay)
+    w = np.asarray(r["w"], np.float32)
+    y = r["y"]
+    ranks = list(range(N)) if ranks is None else list(ranks)
+
+    def one(s):
+        sel = np.flatnonzero((rsrc >= s * T * k) & (rsrc < (s + 1) * T * k))
+        y_sub = bf16_np(_rows(y, sel))
+        comb = O.combine_send(y_sub, rsrc[sel] - s * T * k, 1, T, k)
+        got = bf16_np(B.comb[s])
+        wr = rsrc[sel] - s * T * k
+        assert (got[wr] == comb[wr]).all(), f"comb rank {s}"
+        del got
+        out = O.combine_recv(comb, lay.send_pos[s:s + 1], w[s:s + 1], T, k)[0]
+        check_combine_out(bf16_np(B.out[s]), out)
+        if r.get("out_pull") is not None:
+            check_combine_out(bf16_np(r["out_pull"][s]), out)
+
+    _pmap(one, ranks, 6.0 * T * k * H * 2)
+
+
+def check_partial_full_size(r, lay: O.Layout, ranks=None, bound_every: int = 16, tok_chunk: int = 256):
+    """The send-side partial combine of the source ranks `ranks` (all by
+    default), every token: each group row at its leader's position and the
+    output bit for bit against the oracle's partial_token (run in worker
+    processes, a chunk of tokens each), rows no group leads left untouched,
+    and the mode's tolerance on every bound_every-th token."""
+    import oracle_pool
+    sh = r["sh"]
+    N, T, H, k = sh.N, sh.T, sh.H, sh.k
+    L = sh.E // N
+    comb, out = run_partial(r)
+    w = np.asarray(r["w"], np.float32)
+    ranks = list(range(N)) if ranks is None else list(ranks)
+    items = [(s, t0) for s in ranks for t0 in range(0, T, tok_chunk)]
+
+    def inputs():
+        for s, t0 in items:
+            t1 = min(T, t0 + tok_chunk)
+            em = lay.em_row[s, t0:t1]
+            part = em >= 0
+            rows = bf16_np(_rows(r["y"], np.where(part, em, 0).reshape(-1))).reshape(t1 - t0, k, H)
+            rows[~part] = 0
+            dest = np.where(lay.slot_valid[s, t0:t1], r["idx"][s, t0:t1], 0) // L
+            yield rows, w[s, t0:t1], dest, part
+
+    led = {s: np.zeros(T * k, bool) for s in ranks}
+    got_out = {s: bf16_np(out[s]) for s in ranks}
+    with oracle_pool.pool(oracle_pool.processes()) as pool:
+        for (s, t0), res in zip(items, pool.imap(oracle_pool.partial_tokens, inputs())):
+            pos = [lay.send_pos[s, t0 + i, j] for i, (groups, _) in enumerate(res) for j, _ in groups]
+            got = bf16_np(_rows(comb[s], np.asarray(pos)))
+            want = np.stack([p for groups, _ in res for _, p in groups])
+            assert (got == want).all(), f"group rows, rank {s} tokens {t0}.."
+            led[s][pos] = True
+            for i, (groups, o) in enumerate(res):
+                t = t0 + i
+                assert (got_out[s][t] == o).all(), (s, t)
+                if t % bound_every == 0:
+                    part = lay.em_row[s, t] >= 0
+                    rows_t = bf16_np(_rows(r["y"], np.where(part, lay.em_row[s, t], 0)))
+                    rows_t[~part] = 0
+                    partial_bound_check(got_out[s][t], O.bf16_from_bits(rows_t).astype(np.float64),
+                                        np.where(part, w[s, t], 0.0), [p for _, p in groups])
+    for s in ranks:
+        assert (bf16_np(comb[s])[~led[s]] == PARTIAL_FILL).all(), f"rows no group leads were written (rank {s})"

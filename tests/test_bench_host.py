@@ -60,3 +60,17 @@ def test_more_than_one_gpu_is_refused():
                        cwd=bench.ROOT, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+@pytest.mark.parametrize("N,T,H,E,k,Tc", [(16, 4096, 7168, 256, 8, None), (64, 128, 7168, 384, 8, 4096),
+                                          (4, 7, 256, 8, 3, 5)])
+def test_read_and_written_bytes_add_up_to_the_phase_bytes(N, T, H, E, k, Tc):
+    nb = bench.algorithmic_bytes(N, T, H, E, k, Tc)
+    rw = bench.phase_read_write(N, T, H, E, k, Tc)
+    for p in bench.PHASES:
+        assert sum(rw[p]) == nb[p], p
+    Tcc = T if Tc is None else Tc
+    assert rw["dispatch_recv"][0] == rw["dispatch_recv"][1]          # a permutation: read once, written once
+    assert rw["combine_send"][0] == rw["combine_send"][1]
+    assert rw["combine_recv"][1] == N * Tcc * H * 2                  # one bf16 row per token out
+    assert rw["dispatch_send"][1] > (k / 2) * rw["dispatch_send"][0] * 0.97   # the pack writes about k/2 times what it reads
