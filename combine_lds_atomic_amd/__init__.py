@@ -74,6 +74,7 @@ _SIG = {
     "moe_dispatch_send_ll": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_direct": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_direct_ll": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_direct_noalloc": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_combine_send": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "moe_combine_recv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
@@ -151,6 +152,12 @@ def moe_dispatch_direct_ll(sh, tokens, topk_idx, x_q, x_s, send_pos, exp_off, ro
     _check("moe_dispatch_direct_ll", lib.moe_dispatch_direct_ll(ctypes.byref(sh), _ptr(tokens), _ptr(topk_idx),
                                                                 _ptr(x_q), _ptr(x_s), _ptr(send_pos), _ptr(exp_off),
                                                                 _ptr(row_src), _ptr(ws), _stream(stream)))
+
+
+def moe_dispatch_direct_noalloc(sh, tokens, topk_idx, x_q, x_s, send_pos, exp_off, row_src, flags, stream=None):
+    _check("moe_dispatch_direct_noalloc", lib.moe_dispatch_direct_noalloc(
+        ctypes.byref(sh), _ptr(tokens), _ptr(topk_idx), _ptr(x_q), _ptr(x_s), _ptr(send_pos), _ptr(exp_off),
+        _ptr(row_src), _ptr(flags), _stream(stream)))
 
 
 def moe_dispatch_recv(sh, recv_q, recv_s, ws, x_q, x_s, exp_off, row_src, stream=None):

@@ -14,6 +14,8 @@ int launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t st) {
   return launch("k_fill_u32", k_fill_u32, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, p, v, n);
 }
 
+__global__ void k_copy_u32(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src) { *dst = *src; }
+
 namespace {
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -65,7 +67,9 @@ constexpr size_t kAlign = 256;
 inline size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // Carve the workspace; returns its total size.  ws may be NULL (sizing only).
-size_t carve(const Dims& D, void* ws, Ws* W) {
+// tables_only: only what the multi-launch direct dispatch uses (no unpack
+// row map, no exchange area of the single-launch calls).
+size_t carve(const Dims& D, void* ws, Ws* W, bool tables_only = false) {
   char* b = static_cast<char*>(ws);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -85,10 +89,10 @@ size_t carve(const Dims& D, void* ws, Ws* W) {
   W->exp_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)D.N * (D.L + 1)));
   W->src_in_exp = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(D.N + 1) * D.E));
   W->local = reinterpret_cast<int*>(take(D.B > 1 ? sizeof(int) * (size_t)D.N * D.TK : 0));
-  W->umap = reinterpret_cast<int2*>(take(sizeof(int2) * (size_t)D.rows));
+  W->umap = reinterpret_cast<int2*>(take(tables_only ? 0 : sizeof(int2) * (size_t)D.rows));
   // Exchange area of the single-launch dispatch (one routing chunk per rank
   // only), last so that moe_workspace_init clears it with the header.
-  const bool ll = D.B == 1;
+  const bool ll = D.B == 1 && !tables_only;
   auto take64 = [&](size_t n) { return reinterpret_cast<uint64_t*>(take(ll ? sizeof(uint64_t) * n : 0)); };
   W->ctl = reinterpret_cast<uint32_t*>(take(ll ? sizeof(uint32_t) * (kCtlGroups + 1) * kCtlStride : 0));
   W->tpos = take64((size_t)D.N * D.TK);
@@ -126,6 +130,59 @@ inline Ws W_of(const Dims& D, void* ws) {
   Ws W;
   carve(D, ws, &W);
   return W;
+}
+
+// The workspace of moe_dispatch_direct_noalloc: a file-scope device array,
+// one copy on every GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address: the device address
+// comes from hipGetSymbolAddress, once per device (scratch_address).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on that device (with the device current) and kept per device.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      fprintf(stderr, "libmoe_ep: hipGetSymbolAddress(scratch) failed on device %d: %s\n", dev,
+              hipGetErrorString(e));
+      return MOE_EHIP;
+    }
+    cache[dev] = p;
+  }
+  *out = cache[dev];
+  return MOE_OK;
+}
+
+// The direct dispatch on a carved workspace: routing, then the pack into the
+// expert-major rows (or, without tokens, only the layout).
+int direct_dispatch(const Dims& D, const Ws& W, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* x_q,
+                    float* x_s, int32_t* send_pos, int32_t* exp_off, int32_t* row_src, hipStream_t st) {
+  int rc = launch_route(D, W, topk_idx, send_pos, st);
+  if (rc) return rc;
+  if (D.T == 0)   // the layout-only receive half writes exp_off
+    return launch_unpack(D, W, nullptr, nullptr, nullptr, nullptr, exp_off, row_src, device_cus(), st);
+  return launch_pack(D, W, tokens, topk_idx, send_pos, x_q, x_s, row_src, exp_off, device_cus(), st);
+}
+
+// Host checks of moe_dispatch_direct's arguments (the workspace apart).
+int direct_args(const Dims& D, const uint16_t* tokens, const int32_t* topk_idx, const uint8_t* x_q, const float* x_s,
+                const int32_t* send_pos, const int32_t* exp_off, const int32_t* row_src) {
+  if (!exp_off) return MOE_ENULL;
+  if (!aligned(exp_off, 4)) return MOE_EALIGN;
+  if (D.T == 0) return MOE_OK;   // empty arrays may be NULL
+  if (!topk_idx || !send_pos || !row_src) return MOE_ENULL;
+  if (tokens && (!x_q || !x_s)) return MOE_ENULL;
+  if (!aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(row_src, 4)) return MOE_EALIGN;
+  if (tokens && (!aligned(tokens, 16) || !aligned(x_q, 16) || !aligned(x_s, 4))) return MOE_EALIGN;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -189,22 +246,42 @@ int moe_dispatch_direct(const moe_shape* shape, const uint16_t* tokens, const in
   Dims D;
   int rc = make_dims(shape, &D);
   if (rc) return rc;
-  if (!ws || !exp_off) return MOE_ENULL;
-  if (!aligned(ws, kAlign) || !aligned(exp_off, 4)) return MOE_EALIGN;
-  hipStream_t st = as_stream(stream);
-  Ws W;
-  carve(D, ws, &W);
-  if (D.T == 0) {   // empty arrays may be NULL; the layout-only receive half writes exp_off
-    rc = launch_route(D, W, topk_idx, send_pos, st);
-    return rc ? rc : launch_unpack(D, W, nullptr, nullptr, nullptr, nullptr, exp_off, row_src, device_cus(), st);
-  }
-  if (!topk_idx || !send_pos || !row_src) return MOE_ENULL;
-  if (tokens && (!x_q || !x_s)) return MOE_ENULL;
-  if (!aligned(topk_idx, 4) || !aligned(send_pos, 4) || !aligned(row_src, 4)) return MOE_EALIGN;
-  if (tokens && (!aligned(tokens, 16) || !aligned(x_q, 16) || !aligned(x_s, 4))) return MOE_EALIGN;
-  rc = launch_route(D, W, topk_idx, send_pos, st);
+  if (!ws) return MOE_ENULL;
+  if (!aligned(ws, kAlign)) return MOE_EALIGN;
+  rc = direct_args(D, tokens, topk_idx, x_q, x_s, send_pos, exp_off, row_src);
   if (rc) return rc;
-  return launch_pack(D, W, tokens, topk_idx, send_pos, x_q, x_s, row_src, exp_off, device_cus(), st);
+  return direct_dispatch(D, W_of(D, ws), tokens, topk_idx, x_q, x_s, send_pos, exp_off, row_src, as_stream(stream));
+}
+
+int moe_dispatch_direct_noalloc(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx,
+                                uint8_t* x_q, float* x_s, int32_t* send_pos, int32_t* exp_off, int32_t* row_src,
+                                uint32_t* flags, void* stream) {
+  Dims D;
+  int rc = make_dims(shape, &D);
+  if (rc) return rc;
+  Ws W;
+  const size_t need = carve(D, nullptr, &W, true);
+  if (need > kScratchBytes) {
+    fprintf(stderr, "libmoe_ep: moe_dispatch_direct_noalloc needs %zu bytes of routing tables for this shape, "
+                    "more than its %zu-byte scratch\n", need, kScratchBytes);
+    return MOE_ERANGE;
+  }
+  if (!flags) return MOE_ENULL;
+  if (!aligned(flags, 4)) return MOE_EALIGN;
+  rc = direct_args(D, tokens, topk_idx, x_q, x_s, send_pos, exp_off, row_src);
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  carve(D, ws, &W, true);
+  hipStream_t st = as_stream(stream);
+  // The error word starts at zero for this call (a fill kernel rather than a
+  // memset, so the call can be captured in a graph).
+  rc = launch_fill_u32(W.err, 0u, 1, st);
+  if (rc) return rc;
+  rc = direct_dispatch(D, W, tokens, topk_idx, x_q, x_s, send_pos, exp_off, row_src, st);
+  if (rc) return rc;
+  return launch("k_copy_u32", k_copy_u32, dim3(1), dim3(1), 0, st, flags, static_cast<const uint32_t*>(W.err));
 }
 
 int moe_dispatch_send_ll(const moe_shape* shape, const uint16_t* tokens, const int32_t* topk_idx, uint8_t* recv_q,

@@ -184,6 +184,31 @@ int moe_dispatch_direct(const moe_shape *shape, const uint16_t *tokens, const in
                         float *x_s, int32_t *send_pos, int32_t *exp_off, int32_t *row_src, void *ws, void *stream);
 
 /*
+ * moe_dispatch_direct without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops or
+ * harnesses that forbid hipMalloc): the routing tables live in a 32 MiB
+ * device array of the library's own, one per GPU, set aside when the
+ * library is loaded and held until the process ends.  Nothing is allocated
+ * by the call.  Same arguments, results and limits as moe_dispatch_direct
+ * (bit for bit), with ws replaced by
+ *   flags   uint32 out, device, 4-B aligned: the sticky error bits of this
+ *           call (MOE_FLAG_*), written when the call's work completes.
+ * The tables take about 4 bytes per slot (N*T*k) once a rank has more than
+ * 4096 slots, plus about 4*N*E*(B + 4) bytes with B = the rank's routing
+ * chunks of up to 4096 slots; a shape whose tables exceed 32 MiB is rejected
+ * with MOE_ERANGE before anything is enqueued (a prefill chunk of N = 8,
+ * T = 16384, k = 8, E = 256 needs 4.3 MiB).  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (on different streams) race and
+ * must not be issued; calls on one stream are ordered.  Unlike
+ * moe_dispatch_direct, no workspace tables remain for later calls
+ * (moe_combine_pull, moe_layout_export): the outputs are complete on their
+ * own, and moe_combine_recv needs none.
+ */
+int moe_dispatch_direct_noalloc(const moe_shape *shape, const uint16_t *tokens, const int32_t *topk_idx,
+                                uint8_t *x_q, float *x_s, int32_t *send_pos, int32_t *exp_off, int32_t *row_src,
+                                uint32_t *flags, void *stream);
+
+/*
  * moe_dispatch_direct in a single launch, for decode-sized batches (the
  * low-latency mode of the AWS China blog "750B MoE model migration from a
  * self-built RoCE cluster to AWS EFA", section 4.4: one kernel, no host in

@@ -137,3 +137,15 @@ def test_streams_library_exports_and_rejections():
     assert lib.moe_stream(2, 8, _p(A), _p(A), (1 << 40) + 1, None) == -4   # above 2^40 units
     assert lib.moe_stream(1, 8, None, _p(A), 16, None) == -2
     assert lib.moe_stream(1, 8, _p(A), _p(A + 8), 16, None) == -3
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_on_the_host():
+    """The no-allocation direct dispatch refuses a shape whose routing tables
+    exceed its 32 MiB device array before touching the GPU."""
+    A = 0x10000000
+    big = moe.shape(256, 16384, 128, 1024, 8)          # 33.5M slots: 4 bytes each of in-chunk ranks alone
+    args = [_p(A)] * 7 + [_p(A), None]
+    assert moe.lib.moe_dispatch_direct_noalloc(ctypes.byref(big), *args) == -4
+    small = moe.shape(4, 8, 256, 8, 2)
+    assert moe.lib.moe_dispatch_direct_noalloc(ctypes.byref(small), *([_p(A)] * 7), None, None) == -2   # no flags
+    assert moe.lib.moe_dispatch_direct_noalloc(ctypes.byref(small), *([_p(A)] * 7), _p(A + 2), None) == -3
