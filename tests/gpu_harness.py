@@ -269,22 +269,27 @@ def _rows(t: torch.Tensor, rows: np.ndarray) -> torch.Tensor:
     return t[torch.from_numpy(np.ascontiguousarray(rows, np.int64)).to(t.device)].cpu()
 
 
-def check_dispatch_full_size(r, lay: O.Layout, tok_chunk: int = 1024):
-    """Every receive-region row and every expert-major row (fp8 bytes and fp32
-    scales) against the oracle, chunk by chunk: the oracle quantises each
-    chunk of tokens as the check runs (quantize_rows), and each quantised row
-    must sit, bit for bit, at every row dispatch_send / dispatch_recv put it
-    (recv_row, em_row of the oracle's layout)."""
-    sh, B = r["sh"], r["B"]
+def check_dispatch_full_size(r, lay: O.Layout, tok_chunk: int = 1024, B=None):
+    """Every receive-region row (when B holds them) and every expert-major row
+    (fp8 bytes and fp32 scales) against the oracle, chunk by chunk: the
+    oracle quantises each chunk of tokens as the check runs (quantize_rows),
+    and each quantised row must sit, bit for bit, at every row dispatch_send
+    / dispatch_recv (or the direct dispatch) put it (recv_row, em_row of the
+    oracle's layout)."""
+    sh = r["sh"]
+    B = r["B"] if B is None else B
     N, T, H, k = sh.N, sh.T, sh.H, sh.k
     x = r["x"]
     items = [(s, t0) for s in range(N) for t0 in range(0, T, tok_chunk)]
+    arrays = [("x", lay.em_row, B.x_q, B.x_s)]
+    if B.recv_q is not None:
+        arrays.insert(0, ("recv", lay.recv_row, B.recv_q, B.recv_s))
 
     def one(item):
         s, t0 = item
         t1 = min(T, t0 + tok_chunk)
         q, sc = O.quantize_rows(x[s, t0:t1].float().cpu().numpy())
-        for name, rows, gq, gs in (("recv", lay.recv_row, B.recv_q, B.recv_s), ("x", lay.em_row, B.x_q, B.x_s)):
+        for name, rows, gq, gs in arrays:
             rr = rows[s, t0:t1, :]
             ok = rr >= 0
             got_q = _rows(gq, rr[ok]).numpy()

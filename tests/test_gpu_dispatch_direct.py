@@ -20,7 +20,7 @@ from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import (DIRECT_CALLS, check_layout, check_same_as_two_calls, log, run_all,  # noqa: E402
+from gpu_harness import (DIRECT_CALLS, check_dispatch_full_size, check_layout, check_same_as_two_calls, log, run_all,  # noqa: E402
                          run_direct)
 
 FILL = 0x5A
@@ -213,26 +213,19 @@ def _need(gib):
         pytest.skip(f"needs {gib} GiB of free device memory, {free / 2**30:.0f} GiB free")
 
 
-def _full(cfg, T, n_tok=48, seed=5, call="direct"):
+def _full(cfg, T, call="direct"):
+    """Bit for bit against the two-call path, and every expert-major row
+    against the oracle (chunk by chunk on the host)."""
     if call == "direct_ll" and not _fits_ll(T, cfg.k):
         pytest.skip("the single launch needs T*k <= 4096")
     r = run_all(cfg, T, combine=False)
     B2 = _direct(r, call=call)
     _same_as_two_calls(r, B2)
     sh = r["sh"]
-    N, H, k = sh.N, sh.H, sh.k
-    lay = O.layout(r["idx"], sh.E, N)
+    lay = O.layout(r["idx"], sh.E, sh.N)
     check_layout(dict(r, B=B2), lay)
-    rng = np.random.default_rng(seed)
-    toks = np.unique(np.concatenate([rng.choice(N * T, n_tok, replace=False), [0, N * T - 1]]))
-    s_, t_ = np.divmod(toks, T)
-    xs = r["x"].reshape(N * T, H)[torch.from_numpy(toks).cuda()].float().cpu().numpy()
-    q, sc = O.quantize_rows(xs)
-    rr = lay.em_row[s_, t_, :]
-    ok = rr >= 0
-    ri = torch.from_numpy(rr[ok]).cuda()
-    assert (B2.x_q[ri].cpu().numpy() == np.repeat(q[:, None, :], k, axis=1)[ok]).all()
-    assert (B2.x_s[ri].cpu().numpy().view(np.uint32) == np.repeat(sc[:, None, :], k, axis=1)[ok].view(np.uint32)).all()
+    B2.recv_q = B2.recv_s = None
+    check_dispatch_full_size(r, lay, B=B2)
 
 
 def test_dsv3_decode_full_size(call):
@@ -249,3 +242,36 @@ def test_combine_heavy_full_size():
     _need(30)
     cfg = W.CONFIGS["combine_heavy"]
     _full(cfg, cfg.T)
+
+
+def test_prefill_literal_bound_regions():
+    """The prefill chunk with regions of the literal worst-case size N*T*max(k,
+    E/N) = 4,194,304 rows each ("Send and receive buffers": the receive
+    buffer is sized to that bound), through the direct dispatch, which writes
+    the expert-major rows only: 8 such regions of fp8 rows are 240 GB, which
+    the two-call path (receive regions and expert-major rows) cannot hold in
+    288 GB.  Every integer output and every written row against the oracle."""
+    cfg = W.CONFIGS["prefill"]
+    N, T, H, E, k = cfg.N, cfg.T, cfg.H, cfg.E, cfg.k
+    R = N * T * max(k, cfg.L)
+    sh = moe.shape(N, T, H, E, k, R)
+    rows = moe.moe_recv_rows(sh)
+    need = rows * H + rows * (H // 128) * 4 + rows * 4 + moe.moe_workspace_bytes(sh) + N * T * H * 2
+    free, _ = torch.cuda.mem_get_info()
+    if free < need + (2 << 30):
+        pytest.skip(f"literal-bound regions need {need / 2**30:.1f} GiB of device memory plus 2 GiB of slack, "
+                    f"{free / 2**30:.1f} GiB free")
+    idx, w = W.routing(cfg, T)
+    x = W.tokens(cfg, "cuda", T)
+    B = moe.allocate(sh, "cuda", payload=False, combine=False, fill_rows=-7)
+    B.x_q = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    B.x_s = torch.empty((rows, H // 128), dtype=torch.float32, device="cuda")
+    idx_d = torch.from_numpy(idx).cuda()
+    moe.moe_dispatch_direct(sh, x, idx_d, B.x_q, B.x_s, B.send_pos, B.exp_off, B.row_src, B.ws)
+    flags = moe.moe_status(B.ws)
+    lay = O.layout(idx, E, N, R)
+    assert flags == lay.flags == 0
+    assert lay.recv_total.max() <= R
+    r = dict(sh=sh, idx=idx, w=w, x=x, B=B)
+    check_layout(r, lay)
+    check_dispatch_full_size(r, lay)
