@@ -18,8 +18,8 @@
 //                         side cuts the data sent); one 1024-thread
 //                         workgroup per CU on chunks of tokens,
 //                         thread-interleaved 16-byte units
-//                         (k_comb_send_partial_tokens: one wave per token,
-//                         below 16384 tokens)
+//                         (k_comb_send_partial_os, one-shot, below 16384
+//                         tokens)
 //   k_comb_recv_partial_os  the receive side of it: float32 sum of a token's
 //                         group rows, bf16 out
 #include "moe_internal.h"
@@ -153,17 +153,6 @@ __global__ __launch_bounds__(1024) void k_comb_zero_dropped(Dims D, Ws W, uint16
   zero_dropped_rows<16>(D, W, comb);
 }
 
-// Per lane j < k: whether slot j leads its group, i.e. has a row (dest >= 0)
-// and no earlier slot of the token has a row on the same rank.
-__device__ __forceinline__ bool group_leader(int dest, int k, int lane) {
-  bool lead = dest >= 0;
-  for (int jj = 0; jj < k; ++jj) {
-    const int dj = __builtin_amdgcn_readlane(dest, jj);
-    if (jj < lane && dj == dest) lead = false;
-  }
-  return lead;
-}
-
 enum class CombMode { kRecv, kPull, kRecvPartial };
 
 // The weighted sums, one-shot: one 16-byte output unit (8 elements of a
@@ -208,10 +197,14 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
         row = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
       } else {
         const int e = idx[slot];
-        row = em_row_of(D, W, s, e, sp);
         if constexpr (MODE == CombMode::kRecvPartial) {
-          t_dest[i] = row >= 0 ? e / D.L : -1;
-          row = row >= 0 ? s * D.TK + sp : -1;
+          // Only whether the slot has a row matters here: with packed
+          // regions every valid slot has one, so the lookup is skipped.
+          const bool has = D.R == 0 ? (e >= 0 && e < D.E && sp >= 0 && sp < D.TK) : em_row_of(D, W, s, e, sp) >= 0;
+          t_dest[i] = has ? e / D.L : -1;
+          row = has ? s * D.TK + sp : -1;
+        } else {
+          row = em_row_of(D, W, s, e, sp);
         }
       }
       t_row[i] = row;
@@ -297,109 +290,113 @@ __global__ __launch_bounds__(kOsThreads) void k_comb_recv_partial_os(Dims D, Ws 
   combine_os<CombMode::kRecvPartial, 2>(D, W, comb, idx, send_pos, nullptr, out);
 }
 
-// Send-side partial sums, token by token (one wave per token; the form for
-// problems below 16384 tokens): for each
-// group (a token's slots whose rows sit on one rank) in leader order, its
-// members in slot order, acc = fl(acc + fl(w * y)) with no fused
-// multiply-add, rounded to bf16 and stored where the leader's row returns
-// (comb[s*T*k + send_pos of the leader]).  Each step covers 512 columns
-// (lane l holds 8 elements).  With k <= kSlotGroup (every benchmark shape)
-// a step loads all k rows at once and forms every group from registers;
-// larger k takes the groups one after another, loading each group's
-// members kSlotGroup at a time.  Either way every slot row is read once.
-constexpr int kSpWaves = kSendPartialShape.waves, kSpThreads = kSendPartialShape.threads();
-constexpr int kSendPieces = 2;
-__global__ __launch_bounds__(kSpThreads) void k_comb_send_partial_tokens(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                                   const int* __restrict__ idx,
-                                                                   const int* __restrict__ send_pos,
-                                                                   const float* __restrict__ topk_w,
-                                                                   uint16_t* __restrict__ comb) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  int lo, hi;
-  block_range(D.N * D.T, lo, hi);
-  for (int tok = lo + wv; tok < hi; tok += kSpWaves) {
-    const int s = tok / D.T;
-    int row = -1, dest = -1, sp = -1;
-    float wt = 0.0f;
-    if (lane < D.k) {
-      sp = send_pos[(int64_t)tok * D.k + lane];
-      wt = topk_w[(int64_t)tok * D.k + lane];
-      const int e = idx[(int64_t)tok * D.k + lane];
-      row = em_row_of(D, W, s, e, sp);
-      if (row >= 0) dest = e / D.L;
+// Send-side partial sums, one-shot: one 16-byte unit (8 columns of a token
+// row) per thread.  The tile's tokens have every slot resolved into LDS (its
+// expert-major row, weight, destination rank and, for a group leader, the
+// comb row its group returns to); each thread loads the same 16 bytes of
+// all of its token's slot rows and forms every group's sum from registers
+// (k <= kSlotGroup), or takes the groups one after another (larger k), in
+// slot order as the chunked form does.  The form for fewer than 16384
+// tokens: against the chunked form it took 163 against 188 us at the
+// decode shape and 29 against 45 at the tiny one, but 10.9 against 9.4 ms
+// at the Kimi combine (one process, same buffers); two units per thread
+// were no faster.
+__global__ __launch_bounds__(kOsThreads) void k_comb_send_partial_os(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                                    const int* __restrict__ idx,
+                                                                    const int* __restrict__ send_pos,
+                                                                    const float* __restrict__ topk_w,
+                                                                    uint16_t* __restrict__ comb) {
+  constexpr int U = 1;
+  constexpr int kTile = kOsThreads * U;
+  constexpr int kTab = os_tile_tokens<U>() * kMaxK;
+  __shared__ int t_row[kTab], t_dest[kTab], t_out[kTab];
+  __shared__ float t_w[kTab];
+  const int n16 = D.H / 8, k = D.k;
+  const int64_t units = (int64_t)D.N * D.T * n16;
+  const v4u* __restrict__ ys = reinterpret_cast<const v4u*>(y);
+  v4u* __restrict__ cs = reinterpret_cast<v4u*>(comb);
+  for (int64_t tile = blockIdx.x; tile * kTile < units; tile += gridDim.x) {
+    const int64_t u0 = tile * kTile;
+    int t0, tok, c;
+    os_tile_pos(u0, n16, t0, tok, c);
+    const int64_t ul = u0 + kTile - 1 < units ? u0 + kTile - 1 : units - 1;
+    const int nt = (int)(ul - (int64_t)t0 * n16) / n16 + 1;
+    __syncthreads();   // the previous tile's reads of the tables are done
+    for (int i = threadIdx.x; i < nt * k; i += kOsThreads) {
+      const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
+      const int s = (t0 + i / k) / D.T;
+      const int sp = send_pos[slot];
+      const int e = idx[slot];
+      const int row = em_row_of(D, W, s, e, sp);
+      t_row[i] = row;
+      t_w[i] = topk_w[slot];
+      t_dest[i] = row >= 0 ? e / D.L : -1;
+      t_out[i] = row >= 0 ? s * D.TK + sp : -1;
     }
-    const bool lead = group_leader(dest, D.k, lane);
-    const int orow = lead ? s * D.TK + sp : -1;   // where a leader's group row goes
-    auto weight = [&](int j) {
-      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), j));
-    };
-    if (D.k <= kSlotGroup) {
-      // kSendPieces adjacent 512-column pieces per step: lane l holds
-      // elements [base + c*512 + 8l, +8) of piece c.
-      for (int base = 0; base < D.H; base += kWave * 8 * kSendPieces) {
-        v4u v[kSlotGroup][kSendPieces];
+    __syncthreads();
+    // A slot with a row leads its group unless an earlier slot of the token
+    // has a row on the same rank (reads t_dest only; each entry writes its
+    // own t_out).
+    for (int i = threadIdx.x; i < nt * k; i += kOsThreads) {
+      const int j = i % k, b = i - j, d = t_dest[i];
+      bool lead = d >= 0;
+      for (int jj = 0; jj < j; ++jj) lead = lead && t_dest[b + jj] != d;
+      if (!lead) t_out[i] = -1;
+    }
+    __syncthreads();
+    for (int q = 0; q < U; ++q) {
+      const int64_t uu = u0 + threadIdx.x + q * kOsThreads;
+      if (q > 0) {
+        c += kOsThreads;
+        while (c >= n16) {
+          c -= n16;
+          ++tok;
+        }
+      }
+      if (uu >= units) break;
+      const int b = (tok - t0) * k;
+      if (k <= kSlotGroup) {
+        v4u v[kSlotGroup];
 #pragma unroll
         for (int j = 0; j < kSlotGroup; ++j) {
-          const int r = j < D.k ? __builtin_amdgcn_readlane(row, j) : -1;
-#pragma unroll
-          for (int c = 0; c < kSendPieces; ++c) {
-            const int col = base + c * kWave * 8 + lane * 8;
-            v[j][c] = r >= 0 && col < D.H ? ld16(reinterpret_cast<const v4u*>(y + (int64_t)r * D.H + col))
-                                          : v4u{0, 0, 0, 0};
-          }
+          const int r = j < k ? t_row[b + j] : -1;
+          v[j] = r >= 0 ? ld16(ys + (int64_t)r * n16 + c) : v4u{0, 0, 0, 0};
         }
 #pragma unroll
         for (int g = 0; g < kSlotGroup; ++g) {
-          const int og = g < D.k ? __builtin_amdgcn_readlane(orow, g) : -1;
+          const int og = g < k ? t_out[b + g] : -1;
           if (og < 0) continue;   // not a leader
-          const int dg = __builtin_amdgcn_readlane(dest, g);
-          float acc[kSendPieces][8];
-#pragma unroll
-          for (int c = 0; c < kSendPieces; ++c)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
-#pragma unroll
-          for (int j = g; j < kSlotGroup; ++j) {
-            if (j >= D.k || __builtin_amdgcn_readlane(dest, j) != dg) continue;
-            const float wj = weight(j);
-#pragma unroll
-            for (int c = 0; c < kSendPieces; ++c) acc_row8(acc[c], wj, v[j][c]);
-          }
-#pragma unroll
-          for (int c = 0; c < kSendPieces; ++c) {
-            const int col = base + c * kWave * 8 + lane * 8;
-            if (col < D.H) st16(reinterpret_cast<v4u*>(comb + (int64_t)og * D.H + col), pack_bf16x8(acc[c]));
-          }
-        }
-      }
-    } else {
-      for (int g = 0; g < D.k; ++g) {
-        const int og = __builtin_amdgcn_readlane(orow, g);
-        if (og < 0) continue;
-        const int dg = __builtin_amdgcn_readlane(dest, g);
-        for (int base = 0; base < D.H; base += kWave * 8) {
-          const int col = base + lane * 8;
+          const int dg = t_dest[b + g];
           float acc[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-          for (int j0 = g; j0 < D.k; j0 += kSlotGroup) {
+#pragma unroll
+          for (int j = g; j < kSlotGroup; ++j)
+            if (j < k && t_dest[b + j] == dg) acc_row8(acc, t_w[b + j], v[j]);
+          st16(cs + (int64_t)og * n16 + c, pack_bf16x8(acc));
+        }
+      } else {
+        for (int g = 0; g < k; ++g) {
+          const int og = t_out[b + g];
+          if (og < 0) continue;
+          const int dg = t_dest[b + g];
+          float acc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+          for (int j0 = g; j0 < k; j0 += kSlotGroup) {
             v4u v[kSlotGroup];
             int rr[kSlotGroup];
 #pragma unroll
             for (int jj = 0; jj < kSlotGroup; ++jj) {
               const int j = j0 + jj;
-              rr[jj] = j < D.k && __builtin_amdgcn_readlane(dest, j < D.k ? j : 0) == dg
-                           ? __builtin_amdgcn_readlane(row, j < D.k ? j : 0)
-                           : -1;
-              v[jj] = rr[jj] >= 0 && col < D.H
-                          ? ld16(reinterpret_cast<const v4u*>(y + (int64_t)rr[jj] * D.H + col))
-                          : v4u{0, 0, 0, 0};
+              rr[jj] = j < k && t_dest[b + j] == dg ? t_row[b + j] : -1;
+              v[jj] = rr[jj] >= 0 ? ld16(ys + (int64_t)rr[jj] * n16 + c) : v4u{0, 0, 0, 0};
             }
 #pragma unroll
             for (int jj = 0; jj < kSlotGroup; ++jj)
-              if (rr[jj] >= 0) acc_row8(acc, weight(j0 + jj), v[jj]);
+              if (rr[jj] >= 0) acc_row8(acc, t_w[b + j0 + jj], v[jj]);
           }
-          if (col < D.H) st16(reinterpret_cast<v4u*>(comb + (int64_t)og * D.H + col), pack_bf16x8(acc));
+          st16(cs + (int64_t)og * n16 + c, pack_bf16x8(acc));
         }
       }
     }
@@ -549,9 +546,8 @@ int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, cons
     return launch("k_comb_send_partial", k_comb_send_partial, dim3(grid), dim3(kPsThreads), 0, st, D, W, y,
                   idx, send_pos, w, comb);
   }
-  const int grid = stream_grid(kSendPartialShape, cus, (int64_t)D.N * D.T, kSpWaves);
-  return launch("k_comb_send_partial_tokens", k_comb_send_partial_tokens, dim3(grid), dim3(kSpThreads), 0, st, D, W,
-                y, idx, send_pos, w, comb);
+  return launch("k_comb_send_partial_os", k_comb_send_partial_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8))),
+                dim3(kOsThreads), 0, st, D, W, y, idx, send_pos, w, comb);
 }
 
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,

@@ -182,13 +182,12 @@ __device__ __forceinline__ int region_row(const Dims& D, int s, int u, int recv_
 // ------------------------------------------------------------------ streaming rows
 //
 // The row kernels move gigabytes once, so every bulk access is a 16-byte
-// non-temporal load or store, and every workgroup streams its own contiguous
-// range of rows or tokens: on MI355X a workgroup-contiguous stream sustains
-// ~5.9 TB/s of copy traffic where a fine grid-stride interleave of the same
-// accesses sustains ~5.4 TB/s.  Each kernel has its own launch shape (waves
-// per workgroup, workgroups per CU), measured on the combine-heavy workload.
+// non-temporal load or store.  Most run in the one-shot form below (short
+// workgroups taking consecutive tiles); the chunked forms that remain (the
+// send-side partial sums from 16384 tokens, the single-launch dispatch's
+// packers, the plain streams) give each workgroup a contiguous range and a
+// launch shape of its own (waves per workgroup, workgroups per CU).
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
 
 struct LaunchShape {
   int waves;          // waves per workgroup
@@ -196,8 +195,7 @@ struct LaunchShape {
   constexpr int threads() const { return waves * 64; }
 };
 constexpr LaunchShape kPackShape = {4, 8};          // the single-launch dispatch's packers
-constexpr LaunchShape kSendPartialShape = {16, 1};
-constexpr LaunchShape kCopyShape = {16, 1};
+constexpr LaunchShape kCopyShape = {16, 1};         // the plain streams
 
 // Grid of a streaming kernel of shape S over `items` work units, at most
 // `per_block` of which a workgroup needs to be worth launching.
