@@ -392,6 +392,28 @@ def measure(cfg, args, dev, stream, hip):
             raise SystemExit(f"device error flags {flags_e:#x} in the early-row steps ({cfg.name})")
         del Be, ye, comb_e, out_e
 
+        # The routing alone: both sends without tokens compute only the
+        # layout (send_pos and the tables).  The single launch then runs its
+        # count and cross-rank workgroups only, so its time bounds from above
+        # the routing its packers wait for before their first store (the
+        # cross-rank workgroup's last step, the receive tables, comes after
+        # the packers' signal); the multi-launch send runs its count and
+        # cross-rank kernels.
+        def time_layout(fn):
+            for _ in range(max(args.warmup, 1)):
+                fn(sh, None, idx_d, None, None, B.send_pos, B.ws)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                ev[i][0].record(stream)
+                fn(sh, None, idx_d, None, None, B.send_pos, B.ws)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            t = np.array([e[0].elapsed_time(e[1]) for e in ev])
+            return round(float(np.median(t)) * 1e3, 1)
+
+        single["routing_only_median_us"] = {"moe_dispatch_send_ll": time_layout(moe.moe_dispatch_send_ll),
+                                            "moe_dispatch_send": time_layout(moe.moe_dispatch_send)}
+
     note(f"{cfg.name}: direct dispatch")
     # The direct dispatch (moe_dispatch_direct: rows stored straight at their
     # expert-major rows, no receive regions, no unpack) on the same inputs
@@ -669,6 +691,7 @@ def summary(r):
         "dispatch_send_ll_us": ((r["single_launch_dispatch"] or {}).get("dispatch_send") or {}).get("us"),
         "dispatch_send_ll_early_rows_us": (((r["single_launch_dispatch"] or {}).get("early_rows") or {})
                                            .get("dispatch_send") or {}).get("us"),
+        "routing_only_median_us": (r["single_launch_dispatch"] or {}).get("routing_only_median_us"),
         "combine_partial_us": r["combine_partial"]["us"],
         "vendor_ceilings": {k: v for k, v in r["vendor_ceilings"].items() if k.endswith("GB/s")},
         "pattern_ceilings_GB/s": {p: c["GB/s"] for p, c in r["pattern_ceilings"].items()},

@@ -100,7 +100,6 @@ size_t carve(const Dims& D, void* ws, Ws* W, bool tables_only = false) {
   W->tcnt = take64((size_t)D.N * D.E);
   W->trel = take64((size_t)D.N * D.N);
   W->tbase = take64((size_t)D.N);
-  W->tready = take64((size_t)kReadyCopies * kReadyStride);
   W->tcdone = take64((size_t)D.N * kReadyStride);
   W->temr = take64((size_t)D.N * D.E);
   W->tlim = take64((size_t)D.N * D.N);

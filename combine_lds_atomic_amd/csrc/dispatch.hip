@@ -20,18 +20,19 @@
 //                   nor the unpack are needed
 //   k_dispatch_ll, k_dispatch_ll_direct  the send half (or the direct
 //                   dispatch) in one launch, for decode-sized batches
+#include <algorithm>
 #include <map>
-#include <tuple>
 #include <mutex>
+#include <tuple>
 
 #include "route_dev.h"
 
 
 namespace moe {
 
-constexpr int kPkWaves = kPackShape.waves, kPkThreads = kPackShape.threads();
 constexpr int kPackCols = kWave * 16;         // elements one wave covers per pass (16 per lane)
-constexpr int kPackPasses = 4;                // passes whose loads are issued together
+constexpr int kOsWaves = kOsThreads / kWave;  // pack work items per workgroup
+constexpr int kPackPasses = 4;                // passes whose loads a single-launch packer issues together
 
 // Four quotients x[i] / scale (IEEE division) packed as e4m3fn bytes,
 // little end first.  v_cvt_pk_fp8_f32 converts two floats to OCP e4m3fn
@@ -60,11 +61,11 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ xr, int 
   }
 }
 
-// One pass of a pack work item: this lane's 16 elements at column col (all
-// in one 128-element block shared with 7 neighbouring lanes): block amax,
-// scale, fp8 bytes, the k row stores; the scale goes to the wave's LDS row.
-__device__ __forceinline__ void pack_pass(const Dims& D, const v4u& a, const v4u& b, int col, bool act, int row,
-                                          int lane, uint8_t* __restrict__ recv_q, float* ssw) {
+// This lane's 16 elements as e4m3fn bytes with the scale of their
+// 128-element block: amax over the block (with the 7 neighbouring lanes),
+// scale = amax / 448, q = x / scale.  An all-zero block has scale 0 and zero
+// bytes.  All 64 lanes must call it (cross-lane amax).
+__device__ __forceinline__ v4u quant16(const v4u& a, const v4u& b, float& sc) {
   float v[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -84,7 +85,18 @@ __device__ __forceinline__ void pack_pass(const Dims& D, const v4u& a, const v4u
 #pragma unroll
     for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
   }
-  if (act && (lane & 7) == 0) ssw[col / kScaleBlock] = amax != 0.0f ? scale : 0.0f;
+  sc = amax != 0.0f ? scale : 0.0f;
+  return q;
+}
+
+// One pass of a single-launch pack work item: this lane's 16 elements at
+// column col, quantised and stored to the k rows; the block's scale goes to
+// the wave's LDS row (stored to the rows once per item, 4 bytes per lane).
+__device__ __forceinline__ void pack_pass(const Dims& D, const v4u& a, const v4u& b, int col, bool act, int row,
+                                          int lane, uint8_t* __restrict__ recv_q, float* ssw) {
+  float sc;
+  const v4u q = quant16(a, b, sc);
+  if (act && (lane & 7) == 0) ssw[col / kScaleBlock] = sc;
   for (int j = 0; j < D.k; ++j) {
     const int rj = __builtin_amdgcn_readlane(row, j);
     if (rj >= 0 && act) st16(reinterpret_cast<v4u*>(recv_q + (int64_t)rj * D.H + col), q);
@@ -152,6 +164,37 @@ __device__ __forceinline__ void pack_item(const Dims& D, int item, int row, cons
 }
 
 
+// Pack work item = (token, 1024-element pass), one per wave: lane l holds
+// elements [16l, 16l + 16) of the pass, a 128-element scale block spanning 8
+// lanes.  pack_load reads the lane's 16 bf16 values (zero beyond H) and
+// returns whether it has any.
+__device__ __forceinline__ bool pack_load(const Dims& D, const uint16_t* __restrict__ x, int64_t tok, int col,
+                                          v4u& a, v4u& b) {
+  a = v4u{0, 0, 0, 0};
+  b = v4u{0, 0, 0, 0};
+  if (col >= D.H) return false;
+  const uint16_t* xr = x + tok * D.H + col;
+  a = ld16(reinterpret_cast<const v4u*>(xr));
+  b = ld16(reinterpret_cast<const v4u*>(xr + 8));
+  return true;
+}
+
+// Quantise the lane's 16 elements (quant16) and store them, and from the
+// block's first lane its scale, to the row of every slot j < k (lane j of
+// `row` holds slot j's row, -1 for none).  All 64 lanes must call it.
+__device__ __forceinline__ void pack_store(const Dims& D, const v4u& a, const v4u& b, int col, bool act, int row,
+                                           int lane, uint8_t* __restrict__ q_out, float* __restrict__ s_out) {
+  float sc;
+  const v4u q = quant16(a, b, sc);
+  for (int j = 0; j < D.k; ++j) {
+    const int rj = __builtin_amdgcn_readlane(row, j);
+    if (rj < 0 || !act) continue;
+    st16(reinterpret_cast<v4u*>(q_out + (int64_t)rj * D.H + col), q);
+    if ((lane & 7) == 0) s_out[(int64_t)rj * D.NB + col / kScaleBlock] = sc;
+  }
+}
+
+
 // The row slot i (of rank s's T*k) is packed to, -1 for none.  DIRECT =
 // false: its source-major receive row; DIRECT = true: its expert-major row,
 // by the same index and rule the unpack uses (it exists if both it and its
@@ -200,14 +243,24 @@ __device__ __forceinline__ int pack_slot_row(const Dims& D, const Ws& W, const i
 // AWS EFA", section 4.4, "DeepEP low-latency mode": one kernel per dispatch,
 // no CPU in the loop, capturable in a graph).  The workgroup index gives
 // the role:
-//   b <  N   count rank b's slots (count_chunk) and publish them;
-//   b == N   the cross-rank scans: receive offsets and region bases for the
-//            packers first, then the tables dispatch_recv reads;
-//   b >  N   pack: load tokens while the layout is being computed, then
-//            quantise and store the rows once the positions are known.
+//   b <  N         count rank b's slots (count_chunk) and publish them;
+//   N <= b < 2N    the column of destination rank d = b - N: from the
+//                  counts and send offsets of every source bound for d (one
+//                  round of loads), what a packer needs for d's rows, then
+//                  d's share of the tables dispatch_recv and the combine read;
+//   b == 2N        finish: once every column is out, the scans across
+//                  destinations;
+//   b >  2N        pack: load tokens while the layout is being computed,
+//                  then quantise and store the rows once the positions are
+//                  known.  Packers are as many as fit beside the layout
+//                  workgroups and take the work items interleaved.
+// Splitting the cross-rank work over destinations keeps it to one round of
+// tagged loads per column workgroup; one workgroup doing it all needed a
+// round per few sources (16 rounds at N = 64), which made the routing alone
+// take twice as long as the two routing kernels of moe_dispatch_send.
 // A workgroup only ever waits for values that workgroups with smaller
 // indices produce.  The dispatcher hands each XCD its workgroups in index
-// order, so the N + 1 layout workgroups are the first on their XCDs and are
+// order, so the 2N + 1 layout workgroups are the first on their XCDs and are
 // resident before any packer that could wait for them.  Every wait is also
 // bounded (kSpinLimit): were that order ever not kept, a wait would end with
 // MOE_FLAG_TIMEOUT instead of hanging.  (Taking a ticket from one global
@@ -220,9 +273,10 @@ __device__ __forceinline__ int pack_slot_row(const Dims& D, const Ws& W, const i
 // then the group's signals): on a multi-XCD MI355X a release fence writes
 // back the whole L2 of the XCD, so instead every exchanged value carries the
 // call's tag in the same 8-byte atomic store and is its own completion
-// signal; no fence is issued at all.  The packers poll one of kReadyCopies
-// replicated "ready" words, published after the values they need, then read
-// their values (normally already there, otherwise they keep polling those).
+// signal; no fence is issued at all.  A packer workgroup first waits for
+// one tagged word (a column's completion, or with early rows its rank's
+// count), then reads its values (normally already there, otherwise it keeps
+// polling those).
 
 // v[u] = value at addr(u) for u < n (n <= M), once all carry `tag`; false
 // after kSpinLimit polls.
@@ -271,195 +325,51 @@ __device__ __forceinline__ bool tag_wait3(const uint64_t* p0, const uint64_t* p1
   return true;
 }
 
-// Tagged values the cross-rank role polls at once per thread (register
-// budget: every role of the launch shares the pack role's 64 VGPRs).
-constexpr int kCrossBatch = 4;
+// Tagged values a column thread polls at once (register budget: every role
+// of the launch shares one register allocation).
+constexpr int kColBatch = 4;
 
-// LDS bytes of the cross-rank role.
-inline size_t cross_ll_lds_bytes(int E) { return sizeof(int) * ((size_t)2 * kThreads + E + 1); }
+// LDS ints of the column role: counts, then the senders' offsets per
+// expert, [N][L]; their column scans [N][L]; the senders' offsets to ranks
+// d and d+1, [N] each; the expert totals and their scan [L+1]; 3 totals.
+inline size_t column_ll_lds_bytes(int N, int E) { return sizeof(int) * ((size_t)2 * E + 2 * N + E / N + 4); }
 
-// The cross-rank role: the same tables k_route_cross computes, from the
-// tagged send offsets and counts of the count workgroups.  In the direct
-// form (exp_out != nullptr) the packers need only the column workgroups'
-// values: this role first waits for those and signals the packers, then
-// computes the tables (for moe_layout_export, moe_dispatch_recv's
-// successors and the combine) and copies exp_off to exp_out.
-__device__ void cross_ll(const Dims& D, const Ws& W, uint32_t tag, int* sm, int* wsum, int* exp_out) {
-  const int N = D.N, E = D.E, L = D.L, tid = threadIdx.x;
-  int* part = sm;                  // [G][N], G*N <= kThreads: rows beyond the early ones
-  int* partc = sm + kThreads;      // [G][N]: all rows
-  int* ex = sm + 2 * kThreads;     // [E+1]
-  bool ok = true;
-  if (exp_out) {
-    for (int dd = tid; dd < N && ok; dd += kThreads) {
-      int one;
-      ok = tag_wait(W.tcold + dd * kReadyStride, tag, &one);
-    }
-    __syncthreads();
-    if (tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
-  }
-
-  // (1) rows from source s to destination d are
-  // send_off[s][(d+1)L] - send_off[s][dL]; thread (g, d) sums them over its
-  // share of the sources.
-  const int G = max(1, kThreads / N);
-  const int d = tid % N, g = tid / N;
-  const bool mine = g < G;
-  const int per = (N + G - 1) / G;
-  const int s0 = min(N, g * per), s1 = min(N, s0 + per);
-  const int64_t ld = N + 1;
-  // A thread whose sources fit one batch keeps the values for step (3).
-  int lo1[kCrossBatch] = {}, hi1[kCrossBatch] = {};
-  const bool one = s1 - s0 <= kCrossBatch;
-  if (mine) {
-    int sum = 0, over = 0;
-    for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
-      const int n = min(kCrossBatch, s1 - sb);
-      int lo[kCrossBatch] = {}, hi[kCrossBatch] = {};
-      ok = tag_wait_n(W.toff + sb * ld + d, ld, n, tag, lo) && tag_wait_n(W.toff + sb * ld + d + 1, ld, n, tag, hi);
-#pragma unroll
-      for (int u = 0; u < kCrossBatch; ++u) {
-        sum += hi[u] - lo[u];
-        over += max(hi[u] - lo[u] - D.Ce, 0);
-        lo1[u] = lo[u];
-        hi1[u] = hi[u];
-      }
-    }
-    part[g * N + d] = over;
-    partc[g * N + d] = sum;
-  }
-  __syncthreads();
-  int rt = 0, rover = 0;   // rows received by rank tid; of those, beyond the senders' early rows
-  if (tid < N) {
-    int a = 0;
-    for (int g2 = 0; g2 < G; ++g2) {
-      const int c = part[g2 * N + tid];
-      part[g2 * N + tid] = a;
-      a += c;
-      rt += partc[g2 * N + tid];
-    }
-    rover = a;
-  }
-  // (2) Region bases, rows written per region, capacity and bound checks.
-  int all, vall;
-  const int b = block_scan<kThreads>(rt, wsum, &all);
-  const int vb = block_scan<kThreads>(D.R ? min(rt, D.R) : rt, wsum, &vall);
-  if (tid < N) {
-    const int bd = D.R ? tid * D.R : b;
-    tag_put(W.tbase + tid, tag, bd);
-    W.base[tid] = bd;
-    W.vprefix[tid] = vb;
-    W.recv_total[tid] = rt;
-    W.recv_off[tid * (N + 1) + N] = rover;
-    uint32_t fl = 0;
-    if (D.R && (rt > D.R || D.N * D.Ce + rover > D.R)) fl |= MOE_FLAG_OVERFLOW;
-    if ((int64_t)rt > D.bound) fl |= MOE_FLAG_BOUND;
-    if (fl) atomicOr(W.err, fl);
-  }
-  if (tid == 0) {
-    W.base[N] = D.R ? N * D.R : all;
-    W.vprefix[N] = vall;
-  }
-  // (3) recv_off[d][s], and what a packer of source s adds to a sender
-  // position to get its row inside region d when the row is not one of the
-  // sender's early rows: N*Ce + recv_off[d][s] - Ce - send_off[s][dL].
-  if (mine && ok) {
-    int acc = part[g * N + d];
-    for (int sb = s0; sb < s1 && ok; sb += kCrossBatch) {
-      const int n = min(kCrossBatch, s1 - sb);
-      int lo[kCrossBatch], hi[kCrossBatch];
-#pragma unroll
-      for (int u = 0; u < kCrossBatch; ++u) {
-        lo[u] = lo1[u];
-        hi[u] = hi1[u];
-      }
-      if (!one)
-        ok = tag_wait_n(W.toff + sb * ld + d, ld, n, tag, lo) && tag_wait_n(W.toff + sb * ld + d + 1, ld, n, tag, hi);
-      for (int u = 0; u < n && ok; ++u) {
-        const int s = sb + u;
-        W.recv_off[d * (N + 1) + s] = acc;
-        tag_put(W.trel + (int64_t)s * N + d, tag, N * D.Ce + acc - D.Ce - lo[u]);
-        acc += max(hi[u] - lo[u] - D.Ce, 0);
-      }
-    }
-  }
-  __syncthreads();
-  if (!exp_out && tid < kReadyCopies) tag_put(W.tready + tid * kReadyStride, tag, 1);
-
-  // (4) Off the packers' path: src_in_exp and exp_off for dispatch_recv.
-  for (int e = tid; e < E; e += kThreads) {
-    int acc = 0;
-    for (int sb = 0; sb < N && ok; sb += kCrossBatch) {
-      const int n = min(kCrossBatch, N - sb);
-      int c[kCrossBatch] = {};
-      ok = tag_wait_n(W.tcnt + (int64_t)sb * E + e, E, n, tag, c);
-      for (int u = 0; u < n && ok; ++u) {
-        W.src_in_exp[(sb + u) * E + e] = acc;
-        acc += c[u];
-      }
-    }
-    W.src_in_exp[N * E + e] = acc;
-    ex[e] = acc;
-  }
-  __syncthreads();
-  {
-    // Exclusive scan over all experts, four per thread (E <= 1024).
-    const int e0 = min(E, tid * 4), e1 = min(E, e0 + 4);
-    int v = 0;
-    for (int e = e0; e < e1; ++e) v += ex[e];
-    int etot;
-    int x = block_scan<kThreads>(v, wsum, &etot);
-    for (int e = e0; e < e1; ++e) {
-      const int c = ex[e];
-      ex[e] = x;
-      x += c;
-    }
-    if (tid == 0) ex[E] = etot;
-  }
-  __syncthreads();
-  for (int i = tid; i < N * (L + 1); i += kThreads) {
-    const int dd = i / (L + 1), l = i - dd * (L + 1);
-    W.exp_off[i] = ex[dd * L + l] - ex[dd * L];
-    if (exp_out) exp_out[i] = ex[dd * L + l] - ex[dd * L];
-  }
-  if (!ok) atomicOr(W.err, MOE_FLAG_TIMEOUT);
-}
-
-// LDS ints of the column role: counts, then their column scans, [N][L]
-// each; the senders' offsets to ranks d and d+1, [N] each; the expert
-// totals and their scan [L+1]; the rows beyond the early ones per source,
-// then their scan [N].
-inline size_t column_ll_lds_bytes(int N, int E) { return sizeof(int) * ((size_t)2 * E + 3 * N + E / N + 1); }
-
-// The column role of the direct form, for destination rank d.  From the
-// tagged counts and send offsets alone it publishes what a packer needs for
-// every row bound for d, so the packers do not wait for the cross-rank role:
-//   temr[s][e]  what a packer of source s adds to a sender position of
-//               expert e = d*L + l to get the row's expert-major row,
-//               base[d] + exp_off[d][l] + src_in_exp[s][e] - send_off[s][e]
-//               (packed regions: base[d] = sum over s of send_off[s][d*L],
-//               the slots all sources send to ranks before d);
-//   tlim[s][d]  (fixed regions) the sender positions below which the row's
-//               source-major row fits region d: send_off[s][d*L] + C +
-//               max(0, R - N*C - recv_off[d][s]) with C early rows (0: none);
-// then tcold[d].
-__device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* sm, int* wsum) {
+// The column role for destination rank d.  From the tagged counts of d's
+// experts and the senders' offsets to d and d+1 alone it publishes, for
+// every source s, what a packer adds to a sender position to get the row:
+//   send form:   trel[s][d] = N*C + recv_off[d][s] - C - send_off[s][d*L]
+//                (recv_off: rows beyond the C early ones from sources
+//                before s) and tbase[d] = base[d];
+//   direct form: temr[s][e] = base[d] + exp_off[d][l] + src_in_exp[s][e] -
+//                send_off[s][e] for e = d*L + l, and with fixed regions
+//                tlim[s][d], the sender positions below which the
+//                source-major row fits region d: send_off[s][d*L] + C +
+//                max(0, R - N*C - recv_off[d][s]);
+// packed regions: base[d] = sum over s of send_off[s][d*L] (the slots all
+// sources send to ranks before d).  Then d's part of the workspace tables
+// (recv_off[d], recv_total[d], base[d], src_in_exp and exp_off of d's
+// experts; exp_out too in the direct form) and tcold[d] = rows d receives,
+// published once the packers' values are (in the send form before the
+// tables, which they do not need).
+template <bool DIRECT>
+__device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* sm, int* wsum,
+                          int* __restrict__ exp_out) {
   const int N = D.N, L = D.L, E = D.E, NL = N * L, tid = threadIdx.x;
   int* c = sm;               // [N][L] counts of rank d's experts, then send_off[s][e]
   int* sie = sm + NL;        // [N][L] src_in_exp[s][e]
   int* so0 = sm + 2 * NL;    // [N] send_off[s][d*L]
   int* so1 = so0 + N;        // [N] send_off[s][(d+1)*L]
-  int* ov = so1 + N;         // [N] rows beyond the early ones from s, then recv_off[d][s]
-  int* eo = ov + N;          // [L+1] totals, then exp_off[d][l]
-  // (1) The counts and the senders' offsets, kCrossBatch values per thread
-  // at a time: indices below NL are counts, then send_off[s][d*L], then
+  int* eo = so1 + N;         // [L+1] totals, then exp_off[d][l]
+  int* tot = eo + L + 1;     // [3] rows beyond the early ones, rows, region base
+  // (1) The counts and the senders' offsets, kColBatch values per thread at
+  // a time: indices below NL are counts, then send_off[s][d*L], then
   // send_off[s][(d+1)*L].
   bool ok = true;
   const int nv = NL + 2 * N;
-  for (int i0 = tid * kCrossBatch; i0 < nv && ok; i0 += kThreads * kCrossBatch) {
-    const int n = min(kCrossBatch, nv - i0);
-    int v[kCrossBatch] = {};
-    ok = tag_gather<kCrossBatch>(
+  for (int i0 = tid * kColBatch; i0 < nv && ok; i0 += kThreads * kColBatch) {
+    const int n = min(kColBatch, nv - i0);
+    int v[kColBatch] = {};
+    ok = tag_gather<kColBatch>(
         [&](int u) {
           const int i = i0 + u;
           if (i < NL) return W.tcnt + (int64_t)(i / L) * E + d * L + i % L;
@@ -474,9 +384,7 @@ __device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* 
     }
   }
   const bool fail = __syncthreads_or(!ok);
-  // (2) Per source: rows beyond the early ones; per expert: column scans
-  // over sources.
-  for (int s = tid; s < N && !fail; s += kThreads) ov[s] = max(so1[s] - so0[s] - D.Ce, 0);
+  // (2) Per expert: the column scan over sources.
   for (int l = tid; l < L && !fail; l += kThreads) {
     int acc = 0;
     for (int s = 0; s < N; ++s) {
@@ -484,29 +392,59 @@ __device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* 
       acc += c[s * L + l];
     }
     eo[l] = acc;
+    W.src_in_exp[N * E + d * L + l] = acc;
   }
-  __syncthreads();
-  // (3) Per source: send_off[s][e] over rank d's experts, and recv_off[d][s]
-  // (exclusive scan of the rows beyond the early ones; one thread, N <= 256).
-  for (int s = tid; s < N && !fail; s += kThreads) {
-    int acc = so0[s];
-    for (int l = 0; l < L; ++l) {
-      const int t = c[s * L + l];
-      c[s * L + l] = acc;
-      acc += t;
+  // (3) Per source (one per thread, N <= 256): rows to d, those beyond the
+  // early ones and their scan over sources (recv_off[d][s]); the region base.
+  const int s = tid;
+  const int rows = s < N && !fail ? so1[s] - so0[s] : 0;
+  const int beyond = max(rows - D.Ce, 0);
+  int rover, rt, bd, ro = 0;
+  if (N <= kWave) {   // every source in wave 0: scans without barriers, totals to LDS
+    if (tid < kWave) {
+      ro = wave_scan(beyond, &rover);
+      wave_scan(rows, &rt);
+      wave_scan(s < N && !fail ? so0[s] : 0, &bd);
+      if (tid == 0) {
+        tot[0] = rover;
+        tot[1] = rt;
+        tot[2] = bd;
+      }
+    }
+    __syncthreads();
+    rover = tot[0];
+    rt = tot[1];
+    bd = tot[2];
+  } else {
+    ro = block_scan<kThreads>(beyond, wsum, &rover);
+    block_scan<kThreads>(rows, wsum, &rt);
+    block_scan<kThreads>(s < N && !fail ? so0[s] : 0, wsum, &bd);
+  }
+  if (D.R) bd = d * D.R;
+  if (s < N && !fail) {
+    W.recv_off[d * (N + 1) + s] = ro;
+    if (DIRECT) {
+      if (D.R) tag_put(W.tlim + (int64_t)s * N + d, tag, so0[s] + D.Ce + max(0, D.R - N * D.Ce - ro));
+      int acc = so0[s];   // send_off[s][e] over rank d's experts
+      for (int l = 0; l < L; ++l) {
+        const int t = c[s * L + l];
+        c[s * L + l] = acc;
+        acc += t;
+      }
+    } else {
+      tag_put(W.trel + (int64_t)s * N + d, tag, N * D.Ce + ro - D.Ce - so0[s]);
     }
   }
-  if (tid == 0 && !fail) {
-    int acc = 0;
-    for (int s = 0; s < N; ++s) {
-      const int t = ov[s];
-      ov[s] = acc;
-      acc += t;
+  if (!DIRECT) {
+    // The packers of the send form need nothing more: publish now, the
+    // rest of the tables follow.
+    __syncthreads();
+    if (tid == 0 && !fail) {
+      tag_put(W.tbase + d, tag, bd);
+      tag_put(W.tcold + d * kReadyStride, tag, rt);
     }
   }
-  // (4) exp_off[d][l]: exclusive scan of the totals, four per thread (L <= 1024),
-  // and the packed region base: the sum of send_off[s][d*L] over sources.
-  int bd;
+  // (4) exp_off[d][l]: exclusive scan of the totals, four per thread (L <= 1024).
   {
     const int l0 = min(L, tid * 4), l1 = min(L, l0 + 4);
     int v = 0;
@@ -518,43 +456,64 @@ __device__ void column_ll(const Dims& D, const Ws& W, uint32_t tag, int d, int* 
       eo[l] = x;
       x += t;
     }
-    int b = 0;
-    for (int s = tid; s < N; s += kThreads) b += so0[s];
-    block_scan<kThreads>(b, wsum, &bd);
-    if (D.R) bd = d * D.R;
+    if (tid == 0) eo[L] = all;
   }
   __syncthreads();
   if (!fail) {
-    for (int i = tid; i < NL; i += kThreads) {
-      const int s = i / L, l = i - s * L;
-      tag_put(W.temr + (int64_t)s * E + d * L + l, tag, bd + eo[l] + sie[i] - c[i]);
+    if (DIRECT)
+      for (int i = tid; i < NL; i += kThreads)
+        tag_put(W.temr + (int64_t)(i / L) * E + d * L + i % L, tag, bd + eo[i % L] + sie[i] - c[i]);
+    for (int i = tid; i < NL; i += kThreads) W.src_in_exp[(int64_t)(i / L) * E + d * L + i % L] = sie[i];
+    for (int l = tid; l <= L; l += kThreads) {
+      W.exp_off[d * (L + 1) + l] = eo[l];
+      if (DIRECT) exp_out[d * (L + 1) + l] = eo[l];
     }
-    if (D.R)
-      for (int s = tid; s < N; s += kThreads)
-        tag_put(W.tlim + (int64_t)s * N + d, tag, so0[s] + D.Ce + max(0, D.R - N * D.Ce - ov[s]));
+    if (tid == 0) {
+      W.base[d] = bd;
+      W.recv_total[d] = rt;
+      W.recv_off[d * (N + 1) + N] = rover;
+      uint32_t fl = 0;
+      if (D.R && (rt > D.R || D.N * D.Ce + rover > D.R)) fl |= MOE_FLAG_OVERFLOW;
+      if ((int64_t)rt > D.bound) fl |= MOE_FLAG_BOUND;
+      if (fl) atomicOr(W.err, fl);
+    }
   }
   __syncthreads();
   if (fail) {
     if (tid == 0) atomicOr(W.err, MOE_FLAG_TIMEOUT);
-  } else if (tid == 0) {
-    tag_put(W.tcold + d * kReadyStride, tag, 1);
+  } else if (DIRECT && tid == 0) {
+    tag_put(W.tcold + d * kReadyStride, tag, rt);
   }
 }
 
-static_assert(kPkThreads == kThreads, "the single-launch dispatch runs every role with 256 threads");
+// The finish role: waits for every column (one tagged word each, carrying
+// the rows the destination receives), then the scans across destinations:
+// rows written per region (vprefix) and base[N].
+__device__ void finish_ll(const Dims& D, const Ws& W, uint32_t tag, int* wsum) {
+  const int N = D.N, tid = threadIdx.x;
+  int rt = 0;
+  const bool ok = tid >= N || tag_wait(W.tcold + tid * kReadyStride, tag, &rt);
+  if (__syncthreads_or(!ok)) {
+    if (tid == 0) atomicOr(W.err, MOE_FLAG_TIMEOUT);
+    return;
+  }
+  int all, vall;
+  block_scan<kThreads>(rt, wsum, &all);
+  const int vb = block_scan<kThreads>(D.R ? min(rt, D.R) : rt, wsum, &vall);
+  if (tid < N) W.vprefix[tid] = vb;
+  if (tid == 0) {
+    W.base[N] = D.R ? N * D.R : all;
+    W.vprefix[N] = vall;
+  }
+}
 
-// LDS bytes of the pack role (per-wave scales of one token row).
-inline size_t pack_lds_bytes(int NB) { return sizeof(float) * (size_t)kPkWaves * NB; }
+static_assert(kOsThreads == kThreads, "the single-launch dispatch runs every role with 256 threads");
 
 // The single launch.  DIRECT = false: rows go to the receive regions
-// (recv_q, recv_s).  DIRECT = true: N column workgroups (after the count
-// workgroups, before the cross-rank one) publish, per destination rank,
-// each (source, expert)'s offset into the expert-major layout and the
-// source-major fit limits; the cross-rank workgroup signals the packers once
-// all columns are out, then computes the workspace tables and copies
-// exp_off out; the packers store every row at its expert-major row (recv_q,
-// recv_s = x_q, x_s) and write row_src.  Without tokens (x == nullptr) the
-// direct form still runs its packers, for row_src.
+// (recv_q, recv_s).  DIRECT = true: the packers store every row at its
+// expert-major row (recv_q, recv_s = x_q, x_s) and write row_src, and the
+// columns copy exp_off out.  Without tokens (x == nullptr) the direct form
+// still runs its packers, for row_src; the send form runs none.
 template <bool DIRECT>
 __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
                                             const int* __restrict__ idx, int* __restrict__ send_pos,
@@ -574,34 +533,35 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
   __syncthreads();
   const uint32_t tag = epoch_tag(sh_epoch);
 
-  const int ncol = DIRECT ? D.N : 0;   // column workgroups
   if (wg < D.N) {
     count_chunk(D, W, idx, send_pos, wg, 0, smem, wsum, tag);
     __syncthreads();
     if (threadIdx.x == 0) tag_put(W.tcdone + wg * kReadyStride, tag, 1);
-  } else if (DIRECT && wg < D.N + ncol) {
-    column_ll(D, W, tag, wg - D.N, reinterpret_cast<int*>(smem), wsum);
-  } else if (wg == D.N + ncol) {
-    cross_ll(D, W, tag, reinterpret_cast<int*>(smem), wsum, DIRECT ? exp_out : nullptr);
+  } else if (wg < 2 * D.N) {
+    column_ll<DIRECT>(D, W, tag, wg - D.N, reinterpret_cast<int*>(smem), wsum, exp_out);
+  } else if (wg == 2 * D.N) {
+    finish_ll(D, W, tag, wsum);
   } else {
-    const int p = wg - D.N - ncol - 1;
+    // Packers: work items (token, slice) interleaved over the workgroups
+    // (wave w of packer p takes items 4p + w, then every 4*npack-th), so
+    // the packers resident at any moment cover a compact band of tokens, as
+    // k_pack_os's grid does.
+    const int p = wg - 2 * D.N - 1;
     const int items = D.N * D.T * D.slices;
-    const int lo = (int)((int64_t)items * p / npack), hi = (int)((int64_t)items * (p + 1) / npack);
+    const int stride = npack * kOsWaves;
     bool fail = false;
-    // Without early rows every packer needs the cross-rank results: wait
-    // for a "ready" copy.  With early rows it needs only its own source
-    // ranks' counts for most rows: wait for those ranks' count workgroups.
+    // The workgroup's wait for the layout: one column's word (p % N: the
+    // columns finish together, and the values a packer reads are each
+    // tagged, so this wait only keeps 4 waves per workgroup from polling
+    // them while the layout is computed).  With early rows most rows need
+    // only their own source rank's count: the count workgroup of the rank
+    // of the first item.
     auto gate = [&] {
-      if (threadIdx.x == 0 && lo < hi) {
+      if (threadIdx.x == 0 && p * kOsWaves < items) {
         int one;
-        bool ok;
-        if (DIRECT || D.Ce == 0) {
-          ok = tag_wait(W.tready + (p % kReadyCopies) * kReadyStride, tag, &one);
-        } else {
-          const int s_first = lo / D.slices / D.T, s_last = (hi - 1) / D.slices / D.T;
-          ok = tag_wait(W.tcdone + s_first * kReadyStride, tag, &one) &&
-               tag_wait(W.tcdone + s_last * kReadyStride, tag, &one);
-        }
+        const bool ok = DIRECT || D.Ce == 0
+                            ? tag_wait(W.tcold + (p % D.N) * kReadyStride, tag, &one)
+                            : tag_wait(W.tcdone + (p * kOsWaves / D.slices / D.T) * kReadyStride, tag, &one);
         if (!ok) {
           sh_fail = 1;
           atomicOr(W.err, MOE_FLAG_TIMEOUT);
@@ -610,16 +570,12 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
       __syncthreads();
       fail = sh_fail != 0;
     };
+    const int lane = threadIdx.x & (kWave - 1);
     // Expert of slot j (lane j < k) of work item `item`.
-    auto expert = [&](int item) {
-      const int lane = threadIdx.x & (kWave - 1);
-      const int tok = item / D.slices;
-      return lane < D.k ? idx[(int64_t)tok * D.k + lane] : -1;
-    };
+    auto expert = [&](int item) { return lane < D.k ? idx[(int64_t)(item / D.slices) * D.k + lane] : -1; };
     // Rows of slot j (lane j < k) of work item `item`, expert e, from the
     // tagged positions and offsets.
     auto resolve = [&](int item, int e) {
-      const int lane = threadIdx.x & (kWave - 1);
       const int tok = item / D.slices;
       const int s = tok / D.T;
       int row = -1;
@@ -673,29 +629,28 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     // for the layout, then packs.
     const int wv = threadIdx.x / kWave;
     float* ssw = reinterpret_cast<float*>(smem) + wv * D.NB;
-    int item = lo + wv;
+    int item = p * kOsWaves + wv;
     if (DIRECT && x == nullptr) {   // layout only: positions and row_src
       gate();
-      for (; item < hi; item += kPkWaves) resolve(item, expert(item));
-      item = hi;
+      for (; item < items; item += stride) resolve(item, expert(item));
+      item = items;
     }
-    const bool has = item < hi;
+    const bool has = item < items;
     v4u a[kPackPasses], b[kPackPasses];
     int e1 = -1;
     if (has) {
       int tok, sl, h0, h1;
       item_cols(D, item, tok, sl, h0, h1);
-      load_chunk(x + (int64_t)tok * D.H, h0, h1, threadIdx.x & (kWave - 1), a, b);
+      load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
       e1 = expert(item);
     }
     if (!DIRECT || x != nullptr) gate();
     if (has) {
       pack_item<true>(D, item, resolve(item, e1), x, recv_q, recv_s, ssw, a, b);
-      item += kPkWaves;
+      item += stride;
     }
-    for (; item < hi; item += kPkWaves) pack_item<false>(D, item, resolve(item, expert(item)), x, recv_q, recv_s, ssw);
+    for (; item < items; item += stride) pack_item<false>(D, item, resolve(item, expert(item)), x, recv_q, recv_s, ssw);
   }
-
   // The last workgroup of each group to finish clears the group's counter and
   // counts the group as done; the last group to finish advances every
   // group's call number for the next launch on this workspace (all
@@ -719,8 +674,7 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
 
 __global__ __launch_bounds__(kThreads) void k_dispatch_ll(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                           const int* __restrict__ idx, int* __restrict__ send_pos,
-                                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s,
-                                                          int npack) {
+                                                          uint8_t* __restrict__ recv_q, float* __restrict__ recv_s, int npack) {
   dispatch_ll<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr, npack);
 }
 
@@ -895,52 +849,20 @@ __device__ __forceinline__ void pack_tokens_os(const Dims& D, const Ws& W, const
                                                const int* __restrict__ idx, int* __restrict__ send_pos,
                                                uint8_t* __restrict__ q_out, float* __restrict__ s_out,
                                                int* __restrict__ row_src, int* __restrict__ exp_off) {
-  constexpr int kWavesOs = kOsThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
     for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kOsThreads) exp_off[i] = W.exp_off[i];
   const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;   // layout only: one item per token
   const int64_t items = (int64_t)D.N * D.T * passes;
-  for (int64_t it = (int64_t)blockIdx.x * kWavesOs + wv; it < items; it += (int64_t)gridDim.x * kWavesOs) {
+  for (int64_t it = (int64_t)blockIdx.x * kOsWaves + wv; it < items; it += (int64_t)gridDim.x * kOsWaves) {
     const int tok = (int)(it / passes), pass = (int)(it - (int64_t)tok * passes);
     const int s = tok / D.T, t = tok - s * D.T;
     const int col = pass * kPackCols + lane * 16;    // this lane's 16 elements
-    const bool act = x != nullptr && col < D.H;
-    v4u a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (act) {
-      const uint16_t* xr = x + (int64_t)tok * D.H + col;
-      a = ld16(reinterpret_cast<const v4u*>(xr));
-      b = ld16(reinterpret_cast<const v4u*>(xr + 8));
-    }
+    v4u a, b;
+    const bool act = x != nullptr && pack_load(D, x, tok, col, a, b);
     // Lane j < k resolves slot j.
     const int row = lane < D.k ? pack_slot_row<DIRECT>(D, W, idx, send_pos, row_src, s, t * D.k + lane, pass == 0) : -1;
-    if (x == nullptr) continue;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(a[i]);
-      v[2 * i + 1] = bf16_hi(a[i]);
-      v[8 + 2 * i] = bf16_lo(b[i]);
-      v[8 + 2 * i + 1] = bf16_hi(b[i]);
-    }
-    int am = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = max(am, (int)(__float_as_uint(v[i]) & 0x7FFFFFFFu));
-    am = max8_lanes(am);                     // amax of the 128-element block
-    const float amax = __uint_as_float((uint32_t)am);
-    const float scale = amax / 448.0f;       // IEEE division, round to nearest even
-    v4u q = {0, 0, 0, 0};
-    if (amax != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = quant4(v + 4 * i, scale);
-    }
-    const float sc = amax != 0.0f ? scale : 0.0f;
-    for (int j = 0; j < D.k; ++j) {
-      const int rj = __builtin_amdgcn_readlane(row, j);
-      if (rj < 0 || !act) continue;
-      st16(reinterpret_cast<v4u*>(q_out + (int64_t)rj * D.H + col), q);
-      if ((lane & 7) == 0) s_out[(int64_t)rj * D.NB + col / kScaleBlock] = sc;
-    }
+    if (x != nullptr) pack_store(D, a, b, col, act, row, lane, q_out, s_out);
   }
 }
 
@@ -957,24 +879,14 @@ __global__ __launch_bounds__(kOsThreads) void k_pack_direct_os(Dims D, Ws W, con
   pack_tokens_os<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
 }
 
-// Slices of its hidden dimension each token is split into: doubled while
-// there are fewer work items than the GPU holds waves (about 32 per CU), so
-// small batches still keep enough loads and stores in flight.
-static int pack_slices(const Dims& D, int cus, bool payload) {
-  const int64_t tokens = (int64_t)D.N * D.T;
-  const int passes = (D.H + kPackCols - 1) / kPackCols;
-  const int64_t wave_slots = (int64_t)cus * 32;
-  int sl = 1;
-  if (payload)
-    while (sl * 2 <= passes && tokens * sl * 2 <= wave_slots) sl *= 2;
-  return sl;
-}
-
 int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
                 float* s_out, int* row_src, int* exp_off, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
+  // Without tokens the pack only writes positions: send_pos with several
+  // routing chunks per rank, row_src in the direct form.
+  if (!x && !row_src && D.B == 1) return MOE_OK;
   const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;
-  const int grid = os_grid((int64_t)D.N * D.T * passes, kOsThreads / kWave);
+  const int grid = os_grid((int64_t)D.N * D.T * passes, kOsWaves);
   if (row_src)
     return launch("k_pack_direct_os", k_pack_direct_os, dim3(grid), dim3(kOsThreads), 0, st, D, W, x, idx, send_pos,
                   q_out, s_out, row_src, exp_off);
@@ -990,6 +902,22 @@ int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float
                         ((int64_t)D.rows * ((D.NB & 3) == 0 ? D.NB / 4 : D.NB) + kOsThreads - 1) / kOsThreads;
   return launch("k_unpack_os", k_unpack_os, dim3(os_grid(tiles * kOsThreads)), dim3(kOsThreads), 0, st, D, W,
                 recv_q, recv_s, x_q, x_s);
+}
+
+// Slices of its hidden dimension each token is split into in the single
+// launch's packers: at least 2 (finer items even out the packers' shares:
+// at N = 64, T = 128 whole tokens left the waves 1.46 items each, so half of
+// them did twice the work of the rest), then doubled while there are fewer
+// work items than the GPU holds waves (about 32 per CU), so small batches
+// still keep enough loads and stores in flight.
+static int pack_slices(const Dims& D, int cus, bool payload) {
+  const int64_t tokens = (int64_t)D.N * D.T;
+  const int passes = (D.H + kPackCols - 1) / kPackCols;
+  const int64_t wave_slots = (int64_t)cus * 32;
+  if (!payload) return 1;
+  int sl = passes >= 2 ? 2 : 1;
+  while (sl * 2 <= passes && tokens * sl * 2 <= wave_slots) sl *= 2;
+  return sl;
 }
 
 // Workgroups of k_dispatch_ll to place per CU with `lds` bytes of dynamic
@@ -1019,22 +947,20 @@ int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int
   const bool direct = row_src != nullptr;
   Dims D = D0;
   D.slices = pack_slices(D, cus, x != nullptr);
-  size_t lds = count_lds_bytes(D.E);
-  lds = lds > cross_ll_lds_bytes(D.E) ? lds : cross_ll_lds_bytes(D.E);
-  lds = lds > pack_lds_bytes(D.NB) ? lds : pack_lds_bytes(D.NB);
-  if (direct) lds = lds > column_ll_lds_bytes(D.N, D.E) ? lds : column_ll_lds_bytes(D.N, D.E);
+  // Dynamic LDS: the largest role's (the packers' is a scale row per wave).
+  const size_t lds = std::max({count_lds_bytes(D.E), column_ll_lds_bytes(D.N, D.E),
+                               sizeof(float) * (size_t)kOsWaves * D.NB});
   const void* kernel = direct ? reinterpret_cast<const void*>(k_dispatch_ll_direct)
                               : reinterpret_cast<const void*>(k_dispatch_ll);
-  const int layout_wgs = D.N + 1 + (direct ? D.N : 0);
-  // Packers: one wave per work item (4 per workgroup), at most 8 workgroups
-  // per CU, and no more than fit on the GPU beside the layout workgroups, so
-  // no packer starts late.  The direct form needs packers without tokens too
-  // (they write row_src).
+  const int layout_wgs = 2 * D.N + 1;
+  // Packers: one wave per work item (4 per workgroup), no more than fit on
+  // the GPU beside the layout workgroups, so no packer starts late.  The
+  // direct form needs packers without tokens too (they write row_src).
   int npack = 0;
   if (x || direct) {
-    const int resident = cus * ll_blocks_per_cu(kernel, lds) - layout_wgs;
-    npack = stream_grid(kPackShape, cus, (int64_t)D.N * D.T * D.slices, kPkWaves);
-    if (resident >= 1 && npack > resident) npack = resident;
+    const int64_t need = ((int64_t)D.N * D.T * D.slices + kOsWaves - 1) / kOsWaves;
+    const int64_t resident = (int64_t)cus * ll_blocks_per_cu(kernel, lds) - layout_wgs;
+    npack = (int)std::max<int64_t>(1, std::min(need, resident));
   }
   if (direct)
     return launch("k_dispatch_ll_direct", k_dispatch_ll_direct, dim3(layout_wgs + npack), dim3(kThreads), lds, st, D,

@@ -57,7 +57,7 @@ struct Dims {
   int C;        // routing chunk, slots
   int B;        // routing chunks per rank
   int NB;       // scale blocks per row = H/128
-  int slices;   // pack work items per token (1 = whole row per wave)
+  int slices;   // single-launch pack work items per token (1 = whole row per wave)
   int R;        // fixed region rows, 0 = packed
   int Ce;       // early (private) rows per sender in each fixed region, 0 = none
   int rows;     // rows of every receive / expert-major array
@@ -88,19 +88,16 @@ struct Ws {
   uint64_t *tpos;     // [N*T*k] send positions
   uint64_t *toff;     // [N][N+1] send_off[s][d*L], [s][N] = valid slots of s
   uint64_t *tcnt;     // [N][E] counts
-  uint64_t *trel;     // [N][N] recv_off[d][s] - send_off[s][d*L]
+  uint64_t *trel;     // [N][N] N*C + recv_off[d][s] - C - send_off[s][d*L] (C early rows)
   uint64_t *tbase;    // [N] region bases
-  uint64_t *tready;   // [kReadyCopies][kReadyStride]: published after the values packers need
   uint64_t *tcdone;   // [N][kReadyStride]: rank s's count work is published (early rows)
+  uint64_t *tcold;    // [N][kReadyStride]: the column of destination d is published (value: rows d receives)
   // Direct form only (rows stored at their expert-major rows):
   uint64_t *temr;     // [N][E] base[d] + exp_off[d][l] + src_in_exp[s][e] - send_off[s][e], e = d*L + l
   uint64_t *tlim;     // [N][N] fixed regions: sender positions of s below this fit region d
-  uint64_t *tcold;    // [N][kReadyStride]: the column of destination d is published
 };
 
-// Copies of the "ready" word, one per 64-byte line, so that the waiting
-// workgroups spread their polls over many addresses.
-constexpr int kReadyCopies = 64;
+// Completion words (tcdone, tcold) sit one per 64-byte line.
 constexpr int kReadyStride = 8;
 
 // Control words of the single-launch dispatch.  Workgroup b belongs to group
@@ -183,27 +180,9 @@ __device__ __forceinline__ int region_row(const Dims& D, int s, int u, int recv_
 //
 // The row kernels move gigabytes once, so every bulk access is a 16-byte
 // non-temporal load or store.  Most run in the one-shot form below (short
-// workgroups taking consecutive tiles); the chunked forms that remain (the
-// send-side partial sums from 16384 tokens, the single-launch dispatch's
-// packers, the plain streams) give each workgroup a contiguous range and a
-// launch shape of its own (waves per workgroup, workgroups per CU).
+// workgroups taking consecutive tiles); the send-side partial sums from 16384
+// tokens give each workgroup a contiguous range instead.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
-struct LaunchShape {
-  int waves;          // waves per workgroup
-  int blocks_per_cu;  // workgroups per CU in the grid
-  constexpr int threads() const { return waves * 64; }
-};
-constexpr LaunchShape kPackShape = {4, 8};          // the single-launch dispatch's packers
-constexpr LaunchShape kCopyShape = {16, 1};         // the plain streams
-
-// Grid of a streaming kernel of shape S over `items` work units, at most
-// `per_block` of which a workgroup needs to be worth launching.
-inline int stream_grid(LaunchShape S, int cus, int64_t items, int64_t per_block) {
-  const int64_t need = (items + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)cus * S.blocks_per_cu;
-  return (int)(need < 1 ? 1 : (need < cap ? need : cap));
-}
 
 // Non-temporal on both sides: 3-4% faster than plain accesses on the row
 // kernels, and the fastest of the cache-policy combinations on a copy.

@@ -42,6 +42,20 @@ __device__ int block_scan(int v, int* wsum, int* total) {
   return r;
 }
 
+// Exclusive scan of one value per lane over a wave (no barrier); *total
+// gets the wave total.
+__device__ __forceinline__ int wave_scan(int v, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  *total = __shfl(x, kWave - 1);
+  return x - v;
+}
+
 // LDS bytes count_chunk needs for E experts.
 inline size_t count_lds_bytes(int E) {
   return (size_t)kWavesPerBlock * E * (sizeof(unsigned long long) + sizeof(int));

@@ -1,8 +1,9 @@
 // libmoe_streams (include/moe_streams.h): plain streaming kernels used only
 // as measurement aids beside libmoe_ep.  They move bytes with the row
-// kernels' 16-byte non-temporal accesses and workgroup-contiguous chunks, free
-// of any row lookup or arithmetic, so that the benchmark can give each phase
-// the achievable rate of its own access pattern on its own buffers.
+// kernels' 16-byte non-temporal accesses, free of any row lookup or
+// arithmetic, each in the fastest grid form found for its pattern on
+// MI355X, so that the benchmark can give each phase the achievable rate of
+// its own access pattern on its own buffers.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -11,58 +12,58 @@
 namespace moe {
 namespace {
 
-constexpr int kCpThreads = kCopyShape.threads();
-
-// Plain streaming copy: each workgroup copies one contiguous chunk, every
-// lane with kCopyUnroll loads in flight.  On a 1 GiB copy with one
-// 1024-thread workgroup per CU, 16 loads per lane measured 6.1 TB/s against
-// 6.0 (8), 5.8 (4) and 5.75 (32): the fastest pattern found.
-constexpr int kCopyUnroll = 16;
-__global__ __launch_bounds__(kCpThreads) void k_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                        int64_t n) {
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  constexpr int U = kCopyUnroll;
-  int64_t i = b0 + threadIdx.x;
-  for (; i + (U - 1) * kCpThreads < b1; i += U * kCpThreads) {
-    v4u r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = ld16(src + i + u * kCpThreads);
-#pragma unroll
-    for (int u = 0; u < U; ++u) st16(dst + i + u * kCpThreads, r[u]);
-  }
-  for (; i < b1; i += kCpThreads) st16(dst + i, ld16(src + i));
+// Copy in the one-shot form (one unit per thread, workgroups in address
+// order): 6.5 TB/s on a 4 GiB copy, against 5.6 for the best grid-stride
+// loop and 4.7 for one contiguous chunk per workgroup.
+__global__ __launch_bounds__(kOsThreads) void k_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src,
+                                                       int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kOsThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kOsThreads)
+    st16(dst + i, ld16(src + i));
 }
 
-// The access patterns of the pack and of the receive-side sum: each
-// workgroup a contiguous chunk of units, every thread with all the loads of
-// several units issued together (the fan-out's units past the chunk repeat
-// its last one and store nothing; the reduction's skip their loads, which
-// measured 3.5% faster for it).
+// The access patterns of the pack and of the receive-side sum:
 //   fan-out: unit i reads 32 bytes (src units 2i, 2i+1: a lane's 16 bf16
 //            elements) and stores their XOR at dst unit j*n + i for each
 //            j < K (the k fp8 rows);
 //   reduce:  unit i reads src units j*n + i, j < K (the k slot rows), and
 //            stores their XOR at dst unit i.
-// Units per thread: 4 for the fan-out (8 loads); for the reduction 32/K
-// (32 loads), at most 8: the fastest counts found for plain kernels of
-// these shapes.  (At K = 8 the compiler keeps two of the 16-byte values in
-// scratch; that form measured as fast as a spill-free one.)
+// The reduction runs one-shot (5.8 TB/s at K = 8 against 5.4 for the best
+// chunked form).  The fan-out is the one pattern for which one contiguous
+// chunk per 1024-thread workgroup, one workgroup per CU and 4 units per
+// thread with all 8 loads issued together, measured fastest (5.1 TB/s at
+// K = 8 against 4.8 one-shot).
 template <int K>
-__global__ __launch_bounds__(kCpThreads) void k_stream_fanout(v4u* __restrict__ dst, const v4u* __restrict__ src,
+__global__ __launch_bounds__(kOsThreads) void k_stream_reduce(v4u* __restrict__ dst, const v4u* __restrict__ src,
                                                               int64_t n) {
-  constexpr int U = 4;
+  for (int64_t i = (int64_t)blockIdx.x * kOsThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kOsThreads) {
+    v4u v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = ld16(src + j * n + i);
+    v4u q = v[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) q ^= v[j];
+    st16(dst + i, q);
+  }
+}
+
+constexpr int kFanThreads = 1024, kFanUnits = 4;
+
+template <int K>
+__global__ __launch_bounds__(kFanThreads) void k_stream_fanout(v4u* __restrict__ dst, const v4u* __restrict__ src,
+                                                               int64_t n) {
+  constexpr int U = kFanUnits;
   const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)U * kCpThreads) {
+  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)U * kFanThreads) {
     v4u a[U], b[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = min(i0 + (int64_t)u * kCpThreads, b1 - 1);
+    for (int u = 0; u < U; ++u) {   // units past the chunk repeat its last one and store nothing
+      const int64_t i = min(i0 + (int64_t)u * kFanThreads, b1 - 1);
       a[u] = ld16(src + 2 * i);
       b[u] = ld16(src + 2 * i + 1);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
+      const int64_t i = i0 + (int64_t)u * kFanThreads;
       if (i < b1) {
         const v4u q = a[u] ^ b[u];
 #pragma unroll
@@ -72,39 +73,13 @@ __global__ __launch_bounds__(kCpThreads) void k_stream_fanout(v4u* __restrict__ 
   }
 }
 
-constexpr int stream_reduce_units(int K) { return K <= 3 ? 8 : (K == 4 ? 6 : 32 / K); }   // units per thread
-
-template <int K>
-__global__ __launch_bounds__(kCpThreads) void k_stream_reduce(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                              int64_t n) {
-  constexpr int U = stream_reduce_units(K);
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)U * kCpThreads) {
-    v4u v[U][K];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
-#pragma unroll
-      for (int j = 0; j < K; ++j) v[u][j] = i < b1 ? ld16(src + j * n + i) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v4u q = v[u][0];
-#pragma unroll
-      for (int j = 1; j < K; ++j) q ^= v[u][j];
-      const int64_t i = i0 + (int64_t)u * kCpThreads;
-      if (i < b1) st16(dst + i, q);
-    }
-  }
-}
-
 template <int K>
 int launch_stream_k(int pattern, v4u* dst, const v4u* src, int64_t n16, int cus, hipStream_t st) {
-  const int64_t per_block = (int64_t)kCpThreads * (pattern == MOE_STREAM_FANOUT ? 4 : stream_reduce_units(K));
-  const int grid = stream_grid(kCopyShape, cus, n16, per_block);
-  if (pattern == MOE_STREAM_FANOUT)
-    return launch("k_stream_fanout", k_stream_fanout<K>, dim3(grid), dim3(kCpThreads), 0, st, dst, src, n16);
-  return launch("k_stream_reduce", k_stream_reduce<K>, dim3(grid), dim3(kCpThreads), 0, st, dst, src, n16);
+  if (pattern == MOE_STREAM_REDUCE)
+    return launch("k_stream_reduce", k_stream_reduce<K>, dim3(os_grid(n16)), dim3(kOsThreads), 0, st, dst, src, n16);
+  const int64_t need = (n16 + (int64_t)kFanThreads * kFanUnits - 1) / ((int64_t)kFanThreads * kFanUnits);
+  const int grid = (int)(need < cus ? need : cus);
+  return launch("k_stream_fanout", k_stream_fanout<K>, dim3(grid), dim3(kFanThreads), 0, st, dst, src, n16);
 }
 
 int cus_of_device() {
@@ -136,8 +111,7 @@ int moe_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
   if (!aligned16(dst) || !aligned16(src)) return MOE_EALIGN;
   const int64_t n16 = nbytes / 16;
   if (n16 == 0) return MOE_OK;
-  const int grid = stream_grid(kCopyShape, cus_of_device(), n16, (int64_t)kCpThreads * kCopyUnroll);
-  return launch("k_copy16", k_copy16, dim3(grid), dim3(kCpThreads), 0, static_cast<hipStream_t>(stream),
+  return launch("k_copy16", k_copy16, dim3(os_grid(n16)), dim3(kOsThreads), 0, static_cast<hipStream_t>(stream),
                 reinterpret_cast<v4u*>(dst), reinterpret_cast<const v4u*>(src), n16);
 }
 

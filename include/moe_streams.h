@@ -1,8 +1,9 @@
 /*
  * moe_streams.h -- C ABI of libmoe_streams, a measurement aid that ships
  * beside libmoe_ep and is not part of dispatch / combine: plain streaming
- * kernels with the 16-byte, workgroup-contiguous accesses of the row kernels,
- * free of their row lookups and arithmetic.  The benchmark times them on the
+ * kernels with the 16-byte non-temporal accesses of the row kernels, free of
+ * their row lookups and arithmetic, each in the fastest grid form found for
+ * its access pattern.  The benchmark times them on the
  * phases' own buffers to give each phase the achievable HBM rate of its
  * access pattern on the same GPU, and counter runs use the copy to calibrate
  * the hardware byte counters.
