@@ -230,7 +230,7 @@ class HipRuntime:
             raise RuntimeError(f"hipMemsetAsync returned {rc}")
 
 
-def measure(cfg, args, dev, stream, hip):
+def measure(cfg, args, dev, stream, hip, sweep=False):
     """Every measurement of one workload; returns the result dict and the
     step's total algorithmic bytes and mean step time (ms)."""
     import numpy as np
@@ -589,14 +589,30 @@ def measure(cfg, args, dev, stream, hip):
     vendor_copy = rate(lambda: hip.copy(Bc.comb, y, copy_bytes, stream), 2 * copy_bytes)
     vendor_fill = rate(lambda: hip.fill(Bc.comb, copy_bytes, stream), copy_bytes)
     copy_gbs = rate(lambda: S.moe_copy(Bc.comb, y, copy_bytes), 2 * copy_bytes)
-    fan_gbs = rate(lambda: S.moe_stream(S.STREAM_FANOUT, cfg.k, B.recv_q, x, u_fan), (2 + cfg.k) * u_fan * 16)
+    fan_chunked = rate(lambda: S.moe_stream(S.STREAM_FANOUT, cfg.k, B.recv_q, x, u_fan), (2 + cfg.k) * u_fan * 16)
+    fan_oneshot = rate(lambda: S.moe_stream(S.STREAM_FANOUT_ONESHOT, cfg.k, B.recv_q, x, u_fan),
+                       (2 + cfg.k) * u_fan * 16)
+    fan_gbs = max(fan_chunked, fan_oneshot)    # the faster grid form of the fan-out
     red_gbs = rate(lambda: S.moe_stream(S.STREAM_REDUCE, cfg.k, Bc.out, Bc.comb, u_red), (cfg.k + 1) * u_red * 16)
-    ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays",
-                                  "GB/s": round(fan_gbs, 1)},
+    ceilings = {"dispatch_send": {"pattern": f"fan-out: 32 B read, 16 B stored to each of {cfg.k} arrays "
+                                             "(the faster of two grid forms)",
+                                  "GB/s": round(fan_gbs, 1), "chunked_GB/s": round(fan_chunked, 1),
+                                  "one_shot_GB/s": round(fan_oneshot, 1)},
                 "dispatch_recv": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
                 "combine_send": {"pattern": "copy", "GB/s": round(copy_gbs, 1)},
                 "combine_recv": {"pattern": f"reduction: {cfg.k} arrays read, one stored",
                                  "GB/s": round(red_gbs, 1)}}
+    # The same two streams with fewer arrays (headline workload only): how
+    # much of the fan-out's and the reduction's shortfall against the copy
+    # comes from spreading the accesses over k arrays at once.
+    by_k = None
+    if sweep:
+        by_k = {"fanout_chunked_GB/s": {}, "fanout_one_shot_GB/s": {}, "reduce_GB/s": {}}
+        for kk in sorted({1, 2, 4, cfg.k}):
+            for key, pat in (("fanout_chunked_GB/s", S.STREAM_FANOUT), ("fanout_one_shot_GB/s", S.STREAM_FANOUT_ONESHOT)):
+                by_k[key][kk] = round(rate(lambda: S.moe_stream(pat, kk, B.recv_q, x, u_fan), (2 + kk) * u_fan * 16), 1)
+            by_k["reduce_GB/s"][kk] = round(rate(lambda: S.moe_stream(S.STREAM_REDUCE, kk, Bc.out, Bc.comb, u_red),
+                                                 (kk + 1) * u_red * 16), 1)
     vendor = {"copy_GB/s": round(vendor_copy, 1), "fill_GB/s": round(vendor_fill, 1),
               "bytes": int(copy_bytes),
               "what": "hipMemcpyAsync device-to-device y -> comb (GB/s counts bytes read + written) and "
@@ -662,6 +678,7 @@ def measure(cfg, args, dev, stream, hip):
         "vendor_ceilings": vendor,
         "copy_ceiling_GB/s": round(copy_gbs, 1),
         "pattern_ceilings": ceilings,
+        "pattern_ceilings_by_arrays": by_k,
         "roofline": {"bound": "hbm", "kernel": kernel, "phase": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(kernel, cfg.name)},
@@ -743,7 +760,7 @@ def main():
     hip = HipRuntime()
 
     note(f"gpu: {cfg.name}, {args.warmup} warm-up and {args.steps} timed steps")
-    res, total, step_ms = measure(cfg, args, dev, stream, hip)
+    res, total, step_ms = measure(cfg, args, dev, stream, hip, sweep=True)
     wl = {}
     for name in others:
         note(f"gpu: {name}, {args.warmup} warm-up and {args.steps} timed steps")

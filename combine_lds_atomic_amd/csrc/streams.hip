@@ -28,10 +28,10 @@ __global__ __launch_bounds__(kOsThreads) void k_copy16(v4u* __restrict__ dst, co
 //   reduce:  unit i reads src units j*n + i, j < K (the k slot rows), and
 //            stores their XOR at dst unit i.
 // The reduction runs one-shot (5.8 TB/s at K = 8 against 5.4 for the best
-// chunked form).  The fan-out is the one pattern for which one contiguous
-// chunk per 1024-thread workgroup, one workgroup per CU and 4 units per
-// thread with all 8 loads issued together, measured fastest (5.1 TB/s at
-// K = 8 against 4.8 one-shot).
+// chunked form).  The fan-out comes in both forms: one contiguous chunk per
+// 1024-thread workgroup, one workgroup per CU, 4 units per thread with all
+// 8 loads issued together (5.1 TB/s at K = 8 against 4.9 one-shot), and
+// one-shot, faster for fewer arrays (6.2 TB/s at K = 1 against 5.1).
 template <int K>
 __global__ __launch_bounds__(kOsThreads) void k_stream_reduce(v4u* __restrict__ dst, const v4u* __restrict__ src,
                                                               int64_t n) {
@@ -43,6 +43,16 @@ __global__ __launch_bounds__(kOsThreads) void k_stream_reduce(v4u* __restrict__ 
 #pragma unroll
     for (int j = 1; j < K; ++j) q ^= v[j];
     st16(dst + i, q);
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(kOsThreads) void k_stream_fanout_os(v4u* __restrict__ dst, const v4u* __restrict__ src,
+                                                                 int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kOsThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kOsThreads) {
+    const v4u q = ld16(src + 2 * i) ^ ld16(src + 2 * i + 1);
+#pragma unroll
+    for (int j = 0; j < K; ++j) st16(dst + j * n + i, q);
   }
 }
 
@@ -77,6 +87,9 @@ template <int K>
 int launch_stream_k(int pattern, v4u* dst, const v4u* src, int64_t n16, int cus, hipStream_t st) {
   if (pattern == MOE_STREAM_REDUCE)
     return launch("k_stream_reduce", k_stream_reduce<K>, dim3(os_grid(n16)), dim3(kOsThreads), 0, st, dst, src, n16);
+  if (pattern == MOE_STREAM_FANOUT_ONESHOT)
+    return launch("k_stream_fanout_os", k_stream_fanout_os<K>, dim3(os_grid(n16)), dim3(kOsThreads), 0, st, dst,
+                  src, n16);
   const int64_t need = (n16 + (int64_t)kFanThreads * kFanUnits - 1) / ((int64_t)kFanThreads * kFanUnits);
   const int grid = (int)(need < cus ? need : cus);
   return launch("k_stream_fanout", k_stream_fanout<K>, dim3(grid), dim3(kFanThreads), 0, st, dst, src, n16);
@@ -116,7 +129,8 @@ int moe_copy(void* dst, const void* src, int64_t nbytes, void* stream) {
 }
 
 int moe_stream(int pattern, int k, void* dst, const void* src, int64_t n16, void* stream) {
-  if (pattern != MOE_STREAM_FANOUT && pattern != MOE_STREAM_REDUCE) return MOE_EINVAL;
+  if (pattern != MOE_STREAM_FANOUT && pattern != MOE_STREAM_REDUCE && pattern != MOE_STREAM_FANOUT_ONESHOT)
+    return MOE_EINVAL;
   if (k < 1 || k > 8 || n16 < 0) return MOE_EINVAL;
   if (n16 > ((int64_t)1 << 40)) return MOE_ERANGE;   // keeps n16 * blockIdx within int64 in the kernels
   if (!dst || !src) return MOE_ENULL;

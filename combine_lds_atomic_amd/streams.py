@@ -19,7 +19,7 @@ lib.moe_stream.restype = ctypes.c_int
 lib.moe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                            ctypes.c_void_p]
 
-STREAM_FANOUT, STREAM_REDUCE = 1, 2
+STREAM_FANOUT, STREAM_REDUCE, STREAM_FANOUT_ONESHOT = 1, 2, 3
 
 
 def moe_copy(dst, src, nbytes: int, stream=None):

@@ -37,11 +37,15 @@ int moe_copy(void *dst, const void *src, int64_t nbytes, void *stream);
  *   MOE_STREAM_REDUCE: unit i reads src units j*n16 + i for every j < k and
  *     stores 16 bytes at dst unit i: the receive-side sum's k rows in, one
  *     out.  src holds k*n16 units, dst n16.
+ *   MOE_STREAM_FANOUT_ONESHOT: MOE_STREAM_FANOUT's result from another
+ *     grid (one unit per thread, workgroups in address order), the faster
+ *     form when k is small.
  * Errors: MOE_EINVAL for another pattern, k outside [1, 8] or n16 < 0;
  * MOE_ERANGE for n16 above 2^40 (16 TiB); MOE_ENULL / MOE_EALIGN.
  */
 #define MOE_STREAM_FANOUT 1
 #define MOE_STREAM_REDUCE 2
+#define MOE_STREAM_FANOUT_ONESHOT 3
 int moe_stream(int pattern, int k, void *dst, const void *src, int64_t n16, void *stream);
 
 #ifdef __cplusplus

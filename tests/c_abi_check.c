@@ -50,7 +50,7 @@ int main(void) {
   expect("status without workspace", moe_status(NULL, NULL, &flags), MOE_ENULL);
   expect("copy of a partial 16-byte unit", moe_copy(A, A, 17, NULL), MOE_EINVAL);
   expect("stream with k = 9", moe_stream(MOE_STREAM_REDUCE, 9, A, A, 16, NULL), MOE_EINVAL);
-  expect("stream with another pattern", moe_stream(3, 8, A, A, 16, NULL), MOE_EINVAL);
+  expect("stream with another pattern", moe_stream(4, 8, A, A, 16, NULL), MOE_EINVAL);
 
   if (!fails) printf("c abi ok\n");
   return fails;

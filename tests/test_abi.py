@@ -129,7 +129,7 @@ def test_streams_library_exports_and_rejections():
     lib = S.lib
     assert lib.moe_copy(_p(A), _p(A), 17, None) == -1
     assert lib.moe_copy(_p(A + 1), _p(A), 16, None) == -3
-    assert lib.moe_stream(3, 8, _p(A), _p(A), 16, None) == -1          # no such pattern
+    assert lib.moe_stream(4, 8, _p(A), _p(A), 16, None) == -1          # no such pattern
     assert lib.moe_stream(0, 8, _p(A), _p(A), 16, None) == -1
     assert lib.moe_stream(1, 0, _p(A), _p(A), 16, None) == -1          # k outside [1, 8]
     assert lib.moe_stream(2, 9, _p(A), _p(A), 16, None) == -1
