@@ -301,12 +301,6 @@ __device__ __forceinline__ bool tag_gather(Addr addr, int n, uint32_t tag, int (
   return true;
 }
 
-// v[u] = value of p[u * stride] for u < n (n <= M).
-template <int M>
-__device__ __forceinline__ bool tag_wait_n(const uint64_t* p, int64_t stride, int n, uint32_t tag, int (&v)[M]) {
-  return tag_gather<M>([&](int i) { return p + i * stride; }, n, tag, v);
-}
-
 // Three tagged values at once (p2 may be NULL: v2 is left as it is).
 __device__ __forceinline__ bool tag_wait3(const uint64_t* p0, const uint64_t* p1, const uint64_t* p2, uint32_t tag,
                                           int& v0, int& v1, int& v2) {

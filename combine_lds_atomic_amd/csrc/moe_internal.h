@@ -139,8 +139,6 @@ __device__ __forceinline__ bool tag_wait(const uint64_t* p, uint32_t tag, int* v
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 // One DPP move inside rows of 16 lanes; all lanes active.
 template <int Ctrl>
 __device__ __forceinline__ int dpp_mov(int v) {
@@ -193,25 +191,6 @@ __device__ __forceinline__ void st16(v4u* p, v4u v) { __builtin_nontemporal_stor
 __device__ __forceinline__ void block_range(int n, int& lo, int& hi) {
   lo = (int)((int64_t)n * blockIdx.x / gridDim.x);
   hi = (int)((int64_t)n * (blockIdx.x + 1) / gridDim.x);
-}
-
-// Copy n16 16-byte units from src to dst with the whole wave; each lane
-// issues up to U loads before its stores.
-template <int U>
-__device__ __forceinline__ void wave_copy16(v4u* __restrict__ dst, const v4u* __restrict__ src, int n16, int lane) {
-  for (int c0 = 0; c0 < n16; c0 += kWave * U) {
-    v4u r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave + lane;
-      r[u] = c < n16 ? ld16(src + c) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c < n16) st16(dst + c, r[u]);
-    }
-  }
 }
 
 // One-shot row kernels: one 16-byte unit per thread.  A workgroup of
