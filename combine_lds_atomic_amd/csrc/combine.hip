@@ -162,19 +162,23 @@ enum class CombMode { kRecv, kPull, kRecvPartial };
 // row, with weight 1), then every thread loads the same 16 bytes of each of
 // its token's slot rows and sums them in slot order (acc = fl(acc +
 // fl(w * y)), no fused multiply-add).
-// U output units per thread (tiles of U * kOsThreads units): 1 for the plain
-// and pulling sums; 2 for the sum of group rows, whose slot resolution (the
-// routing-table lookups and the leader pass) costs more per tile and is
-// amortised over twice the units (5-12% faster than 1 from the tiny to the
-// prefill shape; 4 was slower).  For the other two, 2 and 4 were 2-15% slower.
-template <int U>
-constexpr int os_tile_tokens() { return kOsThreads * U / 16 + 2; }   // tokens a tile spans (>= 16 units per row)
-template <CombMode MODE, int U>
+// U output units per thread and TH threads per workgroup (tiles of U * TH
+// units).  U: 1 for the plain sum; 2 for the pulling sum and the sum of
+// group rows, whose slot resolution (the routing-table lookups, the leader
+// pass) costs more per tile and is amortised over twice the units (1-12%
+// faster than 1; 4 was slower; for the plain sum 2 was 1-3% slower except
+// at N = 64).  TH: 64 (one wave per workgroup): 1.5-3% faster than 256 from
+// the decode shape up, 2-3% slower at the tiny shape; 128 was slower than
+// both.
+constexpr int kCombThreads = 64;
+template <int U, int TH>
+constexpr int os_tile_tokens() { return TH * U / 16 + 2; }   // tokens a tile spans (>= 16 units per row)
+template <CombMode MODE, int U, int TH>
 __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uint16_t* __restrict__ rows,
                                            const int* __restrict__ idx, const int* __restrict__ send_pos,
                                            const float* __restrict__ topk_w, uint16_t* __restrict__ out) {
-  constexpr int kTile = kOsThreads * U;
-  constexpr int kOsSlotTable = os_tile_tokens<U>() * kMaxK;
+  constexpr int kTile = TH * U;
+  constexpr int kOsSlotTable = os_tile_tokens<U, TH>() * kMaxK;
   __shared__ int t_row[kOsSlotTable];
   __shared__ float t_w[kOsSlotTable];
   __shared__ int t_dest[MODE == CombMode::kRecvPartial ? kOsSlotTable : 1];
@@ -189,7 +193,7 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
     const int64_t ul = u0 + kTile - 1 < units ? u0 + kTile - 1 : units - 1;
     const int nt = (int)(ul - (int64_t)t0 * n16) / n16 + 1;
     __syncthreads();   // the previous tile's reads of the tables are done
-    for (int i = threadIdx.x; i < nt * k; i += kOsThreads) {
+    for (int i = threadIdx.x; i < nt * k; i += TH) {
       const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
       const int s = (t0 + i / k) / D.T;
       const int sp = send_pos[slot];
@@ -216,11 +220,11 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
       // A slot with a row leads its group unless an earlier slot of the
       // token has a row on the same rank; only leaders' group rows are summed.
       __syncthreads();
-      constexpr int kQ = kOsSlotTable / kOsThreads + 1;
+      constexpr int kQ = kOsSlotTable / TH + 1;
       bool lead[kQ];
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
-        const int i = threadIdx.x + q * kOsThreads;
+        const int i = threadIdx.x + q * TH;
         lead[q] = false;
         if (i < nt * k) {
           const int j = i % k, b = i - j, d = t_dest[i];
@@ -232,15 +236,15 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
-        const int i = threadIdx.x + q * kOsThreads;
+        const int i = threadIdx.x + q * TH;
         if (i < nt * k && !lead[q]) t_row[i] = -1;
       }
     }
     __syncthreads();
     for (int q = 0; q < U; ++q) {
-      const int64_t uu = u0 + threadIdx.x + q * kOsThreads;
-      if (q > 0) {   // this thread's next unit, kOsThreads further on
-        c += kOsThreads;
+      const int64_t uu = u0 + threadIdx.x + q * TH;
+      if (q > 0) {   // this thread's next unit, TH further on
+        c += TH;
         while (c >= n16) {
           c -= n16;
           ++tok;
@@ -269,26 +273,26 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
   }
 }
 
-__global__ __launch_bounds__(kOsThreads) void k_comb_recv_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
+__global__ __launch_bounds__(kCombThreads) void k_comb_recv_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
                                                             const int* __restrict__ send_pos,
                                                             const float* __restrict__ topk_w,
                                                             uint16_t* __restrict__ out) {
-  combine_os<CombMode::kRecv, 1>(D, W, comb, nullptr, send_pos, topk_w, out);
+  combine_os<CombMode::kRecv, 1, kCombThreads>(D, W, comb, nullptr, send_pos, topk_w, out);
 }
 
-__global__ __launch_bounds__(kOsThreads) void k_comb_pull_os(Dims D, Ws W, const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kCombThreads) void k_comb_pull_os(Dims D, Ws W, const uint16_t* __restrict__ y,
                                                             const int* __restrict__ idx,
                                                             const int* __restrict__ send_pos,
                                                             const float* __restrict__ topk_w,
                                                             uint16_t* __restrict__ out) {
-  combine_os<CombMode::kPull, 2>(D, W, y, idx, send_pos, topk_w, out);
+  combine_os<CombMode::kPull, 2, kCombThreads>(D, W, y, idx, send_pos, topk_w, out);
 }
 
-__global__ __launch_bounds__(kOsThreads) void k_comb_recv_partial_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
+__global__ __launch_bounds__(kCombThreads) void k_comb_recv_partial_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
                                                                     const int* __restrict__ idx,
                                                                     const int* __restrict__ send_pos,
                                                                     uint16_t* __restrict__ out) {
-  combine_os<CombMode::kRecvPartial, 2>(D, W, comb, idx, send_pos, nullptr, out);
+  combine_os<CombMode::kRecvPartial, 2, kCombThreads>(D, W, comb, idx, send_pos, nullptr, out);
 }
 
 // Send-side partial sums, one-shot: one 16-byte unit (8 columns of a token
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kOsThreads) void k_comb_send_partial_os(Dims D, Ws 
                                                                     uint16_t* __restrict__ comb) {
   constexpr int U = 1;
   constexpr int kTile = kOsThreads * U;
-  constexpr int kTab = os_tile_tokens<U>() * kMaxK;
+  constexpr int kTab = os_tile_tokens<U, kOsThreads>() * kMaxK;
   __shared__ int t_row[kTab], t_dest[kTab], t_out[kTab];
   __shared__ float t_w[kTab];
   const int n16 = D.H / 8, k = D.k;
@@ -525,18 +529,15 @@ int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* r
 int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, const float* w, uint16_t* out, int cus,
                      hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  return launch("k_comb_recv_os", k_comb_recv_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8))), dim3(kOsThreads),
-                0, st, D, Ws{}, comb, send_pos, w, out);
+  return launch("k_comb_recv_os", k_comb_recv_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), kCombThreads)),
+                dim3(kCombThreads), 0, st, D, Ws{}, comb, send_pos, w, out);
 }
 
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  // Two output units per thread: 1-5% faster than one for the pulling form,
-  // whose slot lookups go through the routing tables (one unit is faster for
-  // the receive from comb, except at N = 64).
-  return launch("k_comb_pull_os", k_comb_pull_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kOsThreads)),
-                dim3(kOsThreads), 0, st, D, W, y, idx, send_pos, w, out);
+  return launch("k_comb_pull_os", k_comb_pull_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kCombThreads)),
+                dim3(kCombThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
 constexpr int64_t kPsMinTokens = 16384;   // tokens (N*T) from which the cooperative form is used
@@ -557,8 +558,9 @@ int launch_comb_send_partial(const Dims& D, const Ws& W, const uint16_t* y, cons
 int launch_comb_recv_partial(const Dims& D, const Ws& W, const uint16_t* comb, const int* idx, const int* send_pos,
                              uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  return launch("k_comb_recv_partial_os", k_comb_recv_partial_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kOsThreads)),
-                dim3(kOsThreads), 0, st, D, W, comb, idx, send_pos, out);
+  return launch("k_comb_recv_partial_os", k_comb_recv_partial_os,
+                dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kCombThreads)), dim3(kCombThreads), 0, st, D, W, comb,
+                idx, send_pos, out);
 }
 
 }  // namespace moe

@@ -31,7 +31,12 @@
 namespace moe {
 
 constexpr int kPackCols = kWave * 16;         // elements one wave covers per pass (16 per lane)
-constexpr int kOsWaves = kOsThreads / kWave;  // pack work items per workgroup
+constexpr int kOsWaves = kOsThreads / kWave;  // one-shot pack work items per workgroup (direct form)
+// k_pack_os: one work item (wave) per workgroup, 1-3.5% faster than four
+// from the decode shape up (2% slower at the tiny shape); the direct form's
+// pack, which also writes row_src, was 1-4% slower with one and keeps four.
+constexpr int kPackWaves = 1;
+constexpr int kLlWaves = kThreads / kWave;    // single-launch packer waves per workgroup
 constexpr int kPackPasses = 4;                // passes whose loads a single-launch packer issues together
 
 // Four quotients x[i] / scale (IEEE division) packed as e4m3fn bytes,
@@ -501,8 +506,6 @@ __device__ void finish_ll(const Dims& D, const Ws& W, uint32_t tag, int* wsum) {
   }
 }
 
-static_assert(kOsThreads == kThreads, "the single-launch dispatch runs every role with 256 threads");
-
 // The single launch.  DIRECT = false: rows go to the receive regions
 // (recv_q, recv_s).  DIRECT = true: the packers store every row at its
 // expert-major row (recv_q, recv_s = x_q, x_s) and write row_src, and the
@@ -542,7 +545,7 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     // k_pack_os's grid does.
     const int p = wg - 2 * D.N - 1;
     const int items = D.N * D.T * D.slices;
-    const int stride = npack * kOsWaves;
+    const int stride = npack * kLlWaves;
     bool fail = false;
     // The workgroup's wait for the layout: one column's word (p % N: the
     // columns finish together, and the values a packer reads are each
@@ -551,11 +554,11 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     // only their own source rank's count: the count workgroup of the rank
     // of the first item.
     auto gate = [&] {
-      if (threadIdx.x == 0 && p * kOsWaves < items) {
+      if (threadIdx.x == 0 && p * kLlWaves < items) {
         int one;
         const bool ok = DIRECT || D.Ce == 0
                             ? tag_wait(W.tcold + (p % D.N) * kReadyStride, tag, &one)
-                            : tag_wait(W.tcdone + (p * kOsWaves / D.slices / D.T) * kReadyStride, tag, &one);
+                            : tag_wait(W.tcdone + (p * kLlWaves / D.slices / D.T) * kReadyStride, tag, &one);
         if (!ok) {
           sh_fail = 1;
           atomicOr(W.err, MOE_FLAG_TIMEOUT);
@@ -623,7 +626,7 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     // for the layout, then packs.
     const int wv = threadIdx.x / kWave;
     float* ssw = reinterpret_cast<float*>(smem) + wv * D.NB;
-    int item = p * kOsWaves + wv;
+    int item = p * kLlWaves + wv;
     if (DIRECT && x == nullptr) {   // layout only: positions and row_src
       gate();
       for (; item < items; item += stride) resolve(item, expert(item));
@@ -771,18 +774,20 @@ __device__ __forceinline__ void unpack_row(const Dims& D, const Ws& W, const Unp
 // 448 payload units (H = 7168) the copy took 1456 us at combine-heavy size,
 // with the two ranges apart 1271 us (the old one-chunk-per-workgroup form:
 // 1411 us).
-__global__ __launch_bounds__(kOsThreads) void k_unpack_index(Dims D, Ws W, int* __restrict__ exp_off,
+constexpr int kIdxThreads = 256;   // k_unpack_index: rows per workgroup (one staging of the region tables)
+
+__global__ __launch_bounds__(kIdxThreads) void k_unpack_index(Dims D, Ws W, int* __restrict__ exp_off,
                                                              int* __restrict__ row_src) {
   __shared__ int svp[kMaxN + 1];
   __shared__ int stage[kStageInts];
-  for (int i = threadIdx.x; i <= D.N; i += kOsThreads) svp[i] = W.vprefix[i];
+  for (int i = threadIdx.x; i <= D.N; i += kIdxThreads) svp[i] = W.vprefix[i];
   if (blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kOsThreads) exp_off[i] = W.exp_off[i];
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kIdxThreads) exp_off[i] = W.exp_off[i];
   __syncthreads();
   const int valid = svp[D.N];
-  for (int64_t lo64 = (int64_t)blockIdx.x * kOsThreads; lo64 < valid; lo64 += (int64_t)gridDim.x * kOsThreads) {
-    const int lo = (int)lo64, hi = min(valid, lo + kOsThreads);
-    const UnpackStage S = unpack_stage<kOsThreads>(D, W, svp, stage, lo, hi);
+  for (int64_t lo64 = (int64_t)blockIdx.x * kIdxThreads; lo64 < valid; lo64 += (int64_t)gridDim.x * kIdxThreads) {
+    const int lo = (int)lo64, hi = min(valid, lo + kIdxThreads);
+    const UnpackStage S = unpack_stage<kIdxThreads>(D, W, svp, stage, lo, hi);
     const int g = lo + (int)threadIdx.x;
     if (g < hi) {
       int src, dst;
@@ -796,26 +801,30 @@ __global__ __launch_bounds__(kOsThreads) void k_unpack_index(Dims D, Ws W, int* 
 __global__ __launch_bounds__(kOsThreads) void k_unpack_os(Dims D, Ws W, const uint8_t* __restrict__ recv_q,
                                                           const float* __restrict__ recv_s, uint8_t* __restrict__ x_q,
                                                           float* __restrict__ x_s) {
+  // Tile width: the workgroup size, 64 or 256 units (the launch chooses), a
+  // power of two, so tiles are counted with shifts (a 64-bit division per
+  // thread made the kernel 2-4% slower).
+  const int lg = __builtin_ctz(blockDim.x);
   const int n16 = D.H / 16;                        // payload units per row
   const bool s16 = (D.NB & 3) == 0;
   const int ns = s16 ? D.NB / 4 : D.NB;
   const int valid = W.vprefix[D.N];
   const int64_t pay = (int64_t)valid * n16;
-  const int64_t ptiles = (pay + kOsThreads - 1) / kOsThreads;
+  const int64_t ptiles = (pay + (1 << lg) - 1) >> lg;
   const int64_t sc = (int64_t)valid * ns;
-  const int64_t tiles = ptiles + (sc + kOsThreads - 1) / kOsThreads;
+  const int64_t tiles = ptiles + ((sc + (1 << lg) - 1) >> lg);
   const v4u* __restrict__ qs = reinterpret_cast<const v4u*>(recv_q);
   v4u* __restrict__ qd = reinterpret_cast<v4u*>(x_q);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     if (tile < ptiles) {
-      const int64_t u0 = tile * kOsThreads;
+      const int64_t u0 = tile << lg;
       if (u0 + threadIdx.x >= pay) continue;
       int g0, g, c;
       os_tile_pos(u0, n16, g0, g, c);
       const int2 m = W.umap[g];
       if (m.x >= 0) st16(qd + (int64_t)m.y * n16 + c, ld16(qs + (int64_t)m.x * n16 + c));
     } else {
-      const int64_t u0 = (tile - ptiles) * kOsThreads;
+      const int64_t u0 = (tile - ptiles) << lg;
       if (u0 + threadIdx.x >= sc) continue;
       int g0, g, c;
       os_tile_pos(u0, ns, g0, g, c);
@@ -838,17 +847,17 @@ __global__ __launch_bounds__(kOsThreads) void k_unpack_os(Dims D, Ws W, const ui
 // block scales to each of the k rows.  The first pass of a token also writes
 // the slot's position when the count kernel left it (several routing chunks
 // per rank), and in the direct form row_src.
-template <bool DIRECT>
+template <bool DIRECT, int WAVES>
 __device__ __forceinline__ void pack_tokens_os(const Dims& D, const Ws& W, const uint16_t* __restrict__ x,
                                                const int* __restrict__ idx, int* __restrict__ send_pos,
                                                uint8_t* __restrict__ q_out, float* __restrict__ s_out,
                                                int* __restrict__ row_src, int* __restrict__ exp_off) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   if (DIRECT && blockIdx.x == 0)   // per-expert offsets for the grouped GEMM, as computed by the scan
-    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += kOsThreads) exp_off[i] = W.exp_off[i];
+    for (int i = threadIdx.x; i < D.N * (D.L + 1); i += WAVES * kWave) exp_off[i] = W.exp_off[i];
   const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;   // layout only: one item per token
   const int64_t items = (int64_t)D.N * D.T * passes;
-  for (int64_t it = (int64_t)blockIdx.x * kOsWaves + wv; it < items; it += (int64_t)gridDim.x * kOsWaves) {
+  for (int64_t it = (int64_t)blockIdx.x * WAVES + wv; it < items; it += (int64_t)gridDim.x * WAVES) {
     const int tok = (int)(it / passes), pass = (int)(it - (int64_t)tok * passes);
     const int s = tok / D.T, t = tok - s * D.T;
     const int col = pass * kPackCols + lane * 16;    // this lane's 16 elements
@@ -860,17 +869,17 @@ __device__ __forceinline__ void pack_tokens_os(const Dims& D, const Ws& W, const
   }
 }
 
-__global__ __launch_bounds__(kOsThreads) void k_pack_os(Dims D, Ws W, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kPackWaves * kWave) void k_pack_os(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                         const int* __restrict__ idx, int* __restrict__ send_pos,
                                                         uint8_t* __restrict__ recv_q, float* __restrict__ recv_s) {
-  pack_tokens_os<false>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
+  pack_tokens_os<false, kPackWaves>(D, W, x, idx, send_pos, recv_q, recv_s, nullptr, nullptr);
 }
 
 __global__ __launch_bounds__(kOsThreads) void k_pack_direct_os(Dims D, Ws W, const uint16_t* __restrict__ x,
                                                                const int* __restrict__ idx, int* __restrict__ send_pos,
                                                                uint8_t* __restrict__ x_q, float* __restrict__ x_s,
                                                                int* __restrict__ row_src, int* __restrict__ exp_off) {
-  pack_tokens_os<true>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
+  pack_tokens_os<true, kOsWaves>(D, W, x, idx, send_pos, x_q, x_s, row_src, exp_off);
 }
 
 int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, int* send_pos, uint8_t* q_out,
@@ -879,23 +888,27 @@ int launch_pack(const Dims& D, const Ws& W, const uint16_t* x, const int* idx, i
   // Without tokens the pack only writes positions: send_pos with several
   // routing chunks per rank, row_src in the direct form.
   if (!x && !row_src && D.B == 1) return MOE_OK;
-  const int passes = x ? (D.H + kPackCols - 1) / kPackCols : 1;
-  const int grid = os_grid((int64_t)D.N * D.T * passes, kOsWaves);
+  const int64_t items = (int64_t)D.N * D.T * (x ? (D.H + kPackCols - 1) / kPackCols : 1);
   if (row_src)
-    return launch("k_pack_direct_os", k_pack_direct_os, dim3(grid), dim3(kOsThreads), 0, st, D, W, x, idx, send_pos,
-                  q_out, s_out, row_src, exp_off);
-  return launch("k_pack_os", k_pack_os, dim3(grid), dim3(kOsThreads), 0, st, D, W, x, idx, send_pos, q_out, s_out);
+    return launch("k_pack_direct_os", k_pack_direct_os, dim3(os_grid(items, kOsWaves)), dim3(kOsThreads), 0, st, D, W,
+                  x, idx, send_pos, q_out, s_out, row_src, exp_off);
+  return launch("k_pack_os", k_pack_os, dim3(os_grid(items, kPackWaves)), dim3(kPackWaves * kWave), 0, st, D, W, x,
+                idx, send_pos, q_out, s_out);
 }
 
 int launch_unpack(const Dims& D, const Ws& W, const uint8_t* recv_q, const float* recv_s, uint8_t* x_q, float* x_s,
                   int* exp_off, int* row_src, int cus, hipStream_t st) {
-  const int rc = launch("k_unpack_index", k_unpack_index, dim3(os_grid(D.rows)), dim3(kOsThreads), 0, st, D, W,
+  const int rc = launch("k_unpack_index", k_unpack_index, dim3(os_grid(D.rows, kIdxThreads)), dim3(kIdxThreads), 0, st, D, W,
                         exp_off, row_src);
   if (rc != MOE_OK || x_q == nullptr || D.rows == 0) return rc;   // layout only
-  const int64_t tiles = ((int64_t)D.rows * (D.H / 16) + kOsThreads - 1) / kOsThreads +
-                        ((int64_t)D.rows * ((D.NB & 3) == 0 ? D.NB / 4 : D.NB) + kOsThreads - 1) / kOsThreads;
-  return launch("k_unpack_os", k_unpack_os, dim3(os_grid(tiles * kOsThreads)), dim3(kOsThreads), 0, st, D, W,
-                recv_q, recv_s, x_q, x_s);
+  // Tiles of 64 units (one wave per workgroup) from 2^26 payload units up
+  // (a 1-1.6% gain at the combine-heavy and prefill sizes), of 256 below
+  // (64 was 1-1.4% slower at the decode, Kimi-dispatch and tiny sizes).
+  const int64_t pay = (int64_t)D.rows * (D.H / 16);
+  const int th = pay >= ((int64_t)1 << 26) ? 64 : kOsThreads;
+  const int64_t tiles = (pay + th - 1) / th + ((int64_t)D.rows * ((D.NB & 3) == 0 ? D.NB / 4 : D.NB) + th - 1) / th;
+  return launch("k_unpack_os", k_unpack_os, dim3(os_grid(tiles * th, th)), dim3(th), 0, st, D, W, recv_q, recv_s, x_q,
+                x_s);
 }
 
 // Slices of its hidden dimension each token is split into in the single
@@ -943,7 +956,7 @@ int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int
   D.slices = pack_slices(D, cus, x != nullptr);
   // Dynamic LDS: the largest role's (the packers' is a scale row per wave).
   const size_t lds = std::max({count_lds_bytes(D.E), column_ll_lds_bytes(D.N, D.E),
-                               sizeof(float) * (size_t)kOsWaves * D.NB});
+                               sizeof(float) * (size_t)kLlWaves * D.NB});
   const void* kernel = direct ? reinterpret_cast<const void*>(k_dispatch_ll_direct)
                               : reinterpret_cast<const void*>(k_dispatch_ll);
   const int layout_wgs = 2 * D.N + 1;
@@ -952,7 +965,7 @@ int launch_dispatch_ll(const Dims& D0, const Ws& W, const uint16_t* x, const int
   // direct form needs packers without tokens too (they write row_src).
   int npack = 0;
   if (x || direct) {
-    const int64_t need = ((int64_t)D.N * D.T * D.slices + kOsWaves - 1) / kOsWaves;
+    const int64_t need = ((int64_t)D.N * D.T * D.slices + kLlWaves - 1) / kLlWaves;
     const int64_t resident = (int64_t)cus * ll_blocks_per_cu(kernel, lds) - layout_wgs;
     npack = (int)std::max<int64_t>(1, std::min(need, resident));
   }
