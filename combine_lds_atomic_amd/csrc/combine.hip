@@ -103,48 +103,36 @@ __device__ void zero_dropped_rows(const Dims& D, const Ws& W, uint16_t* __restri
 }
 
 // ------------------------------------------------------------------ one-shot forms
-constexpr int kOsMaxTileRows = kOsThreads / 16 + 2;     // rows a tile spans (at least 16 units per row)
 
 // Combine send, one-shot: comb[row_src[p]] = y[p] over the valid rows
-// (region order), one 16-byte unit per thread.  The tile's rows are resolved
-// into LDS first (physical row, and its comb row from row_src).
-__global__ __launch_bounds__(kOsThreads) void k_comb_send_os(Dims D, Ws W, const uint16_t* __restrict__ y,
-                                                            const int* __restrict__ row_src,
-                                                            uint16_t* __restrict__ comb) {
-  __shared__ int t_src[kOsMaxTileRows], t_dst[kOsMaxTileRows];
+// (region order), one 16-byte unit per thread, 64-thread workgroups.  Each
+// thread looks its row up itself (the row's 896 units at H = 7168 share the
+// row_src entry in the cache).  Against 256-thread tiles that first resolved
+// their rows into LDS: 4% faster at combine-heavy size, 0.3-2.5% at the
+// others.
+constexpr int kSendThreads = 64;
+__global__ __launch_bounds__(kSendThreads) void k_comb_send_os(Dims D, Ws W, const uint16_t* __restrict__ y,
+                                                              const int* __restrict__ row_src,
+                                                              uint16_t* __restrict__ comb) {
   const int n16 = D.H / 8;
   const int valid = W.vprefix[D.N];
   const int64_t units = (int64_t)valid * n16;
   const int ncomb = D.N * D.TK;
   const v4u* __restrict__ ys = reinterpret_cast<const v4u*>(y);
   v4u* __restrict__ cs = reinterpret_cast<v4u*>(comb);
-  for (int64_t tile = blockIdx.x; tile * kOsThreads < units; tile += gridDim.x) {
-    const int64_t u0 = tile * kOsThreads;
+  for (int64_t tile = blockIdx.x; tile * kSendThreads < units; tile += gridDim.x) {
+    const int64_t u0 = tile * kSendThreads;
+    if (u0 + threadIdx.x >= units) continue;
     int g0, g, c;
     os_tile_pos(u0, n16, g0, g, c);
-    const int64_t ul = u0 + kOsThreads - 1 < units ? u0 + kOsThreads - 1 : units - 1;
-    const int nr = (int)(ul - (int64_t)g0 * n16) / n16 + 1;
-    __syncthreads();   // the previous tile's reads of the table are done
-    for (int i = threadIdx.x; i < nr; i += kOsThreads) {
-      const int gi = g0 + i;
-      int p = gi;                                  // packed regions: valid row gi is physical row gi
-      if (D.R) {
-        const int d = floor_index(W.vprefix, D.N + 1, gi);
-        p = W.base[d] + (gi - W.vprefix[d]);
-      }
-      int dst = -1;
-      if (p < D.rows) {
-        const int rs = row_src[p];
-        if (rs >= 0 && rs < ncomb) dst = rs;
-      }
-      t_src[i] = dst >= 0 ? p : -1;
-      t_dst[i] = dst;
+    int p = g;                                     // packed regions: valid row g is physical row g
+    if (D.R) {
+      const int d = floor_index(W.vprefix, D.N + 1, g);
+      p = W.base[d] + (g - W.vprefix[d]);
     }
-    __syncthreads();
-    if (u0 + threadIdx.x < units) {
-      const int r = g - g0;
-      if (t_src[r] >= 0) st16(cs + (int64_t)t_dst[r] * n16 + c, ld16(ys + (int64_t)t_src[r] * n16 + c));
-    }
+    if (p >= D.rows) continue;
+    const int rs = row_src[p];
+    if (rs >= 0 && rs < ncomb) st16(cs + (int64_t)rs * n16 + c, ld16(ys + (int64_t)p * n16 + c));
   }
 }
 
@@ -154,20 +142,18 @@ __global__ __launch_bounds__(1024) void k_comb_zero_dropped(Dims D, Ws W, uint16
   zero_dropped_rows<16>(D, W, comb);
 }
 
-enum class CombMode { kRecv, kPull, kRecvPartial };
+enum class CombMode { kPull, kRecvPartial };
 
-// The weighted sums, one-shot: one 16-byte output unit (8 elements of a
-// token row) per thread.  The tile's tokens have their slots resolved into
-// LDS first (slot row, weight; for kRecvPartial only group leaders keep a
+// The pulling sum and the sum of group rows, one-shot: one 16-byte output
+// unit (8 elements of a token row) per thread.  The tile's tokens have their
+// slots resolved into LDS first (slot row, weight; for kRecvPartial only group leaders keep a
 // row, with weight 1), then every thread loads the same 16 bytes of each of
 // its token's slot rows and sums them in slot order (acc = fl(acc +
 // fl(w * y)), no fused multiply-add).
 // U output units per thread and TH threads per workgroup (tiles of U * TH
-// units).  U: 1 for the plain sum; 2 for the pulling sum and the sum of
-// group rows, whose slot resolution (the routing-table lookups, the leader
-// pass) costs more per tile and is amortised over twice the units (1-12%
-// faster than 1; 4 was slower; for the plain sum 2 was 1-3% slower except
-// at N = 64).  TH: 64 (one wave per workgroup): 1.5-3% faster than 256 from
+// units).  U = 2: the slot resolution (the routing-table lookups, the leader
+// pass) is amortised over twice the units (1-12% faster than 1; 4 was
+// slower).  TH = 64 (one wave per workgroup): 1.5-3% faster than 256 from
 // the decode shape up, 2-3% slower at the tiny shape; 128 was slower than
 // both.
 constexpr int kCombThreads = 64;
@@ -197,20 +183,16 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
       const int64_t slot = (int64_t)t0 * k + i;               // token t0 + i / k, slot i % k
       const int s = (t0 + i / k) / D.T;
       const int sp = send_pos[slot];
+      const int e = idx[slot];
       int row;
-      if constexpr (MODE == CombMode::kRecv) {
-        row = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
+      if constexpr (MODE == CombMode::kRecvPartial) {
+        // Only whether the slot has a row matters here: with packed
+        // regions every valid slot has one, so the lookup is skipped.
+        const bool has = D.R == 0 ? (e >= 0 && e < D.E && sp >= 0 && sp < D.TK) : em_row_of(D, W, s, e, sp) >= 0;
+        t_dest[i] = has ? e / D.L : -1;
+        row = has ? s * D.TK + sp : -1;
       } else {
-        const int e = idx[slot];
-        if constexpr (MODE == CombMode::kRecvPartial) {
-          // Only whether the slot has a row matters here: with packed
-          // regions every valid slot has one, so the lookup is skipped.
-          const bool has = D.R == 0 ? (e >= 0 && e < D.E && sp >= 0 && sp < D.TK) : em_row_of(D, W, s, e, sp) >= 0;
-          t_dest[i] = has ? e / D.L : -1;
-          row = has ? s * D.TK + sp : -1;
-        } else {
-          row = em_row_of(D, W, s, e, sp);
-        }
+        row = em_row_of(D, W, s, e, sp);
       }
       t_row[i] = row;
       if constexpr (MODE == CombMode::kRecvPartial) t_w[i] = 1.0f;
@@ -273,11 +255,61 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
   }
 }
 
+// The plain sum, one 16-byte output unit (8 elements of token tok, column
+// unit c) per thread, each thread looking its token's slots up itself: the
+// 64 threads of a workgroup mostly share one token, so the lookups are cache
+// hits.  Against tiles that first resolved their tokens' slots into LDS: 3-8%
+// faster from the decode shape up (0.7 us slower at the tiny shape).  The
+// pulling sum keeps the LDS tiles: its per-slot routing-table lookup done by
+// every thread was twice as slow.
+__device__ __forceinline__ v4u recv_unit(const Dims& D, const v4u* __restrict__ rs, const int* __restrict__ send_pos,
+                                         const float* __restrict__ topk_w, int tok, int c) {
+  const int n16 = D.H / 8, k = D.k, s = tok / D.T;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+    v4u v[kSlotGroup];
+    int rr[kSlotGroup];
+    float ww[kSlotGroup];
+#pragma unroll
+    for (int jj = 0; jj < kSlotGroup; ++jj) {
+      const int j = j0 + jj;
+      rr[jj] = -1;
+      ww[jj] = 0.0f;
+      if (j < k) {
+        const int64_t slot = (int64_t)tok * k + j;
+        const int sp = send_pos[slot];
+        rr[jj] = sp >= 0 && sp < D.TK ? s * D.TK + sp : -1;
+        ww[jj] = topk_w[slot];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kSlotGroup; ++jj) v[jj] = rr[jj] >= 0 ? ld16(rs + (int64_t)rr[jj] * n16 + c) : v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int jj = 0; jj < kSlotGroup; ++jj)
+      if (rr[jj] >= 0) acc_row8(acc, ww[jj], v[jj]);
+  }
+  return pack_bf16x8(acc);
+}
+
+constexpr int kPullUnits = 2;   // output units per thread of the pulling sum
+
 __global__ __launch_bounds__(kCombThreads) void k_comb_recv_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
                                                             const int* __restrict__ send_pos,
                                                             const float* __restrict__ topk_w,
                                                             uint16_t* __restrict__ out) {
-  combine_os<CombMode::kRecv, 1, kCombThreads>(D, W, comb, nullptr, send_pos, topk_w, out);
+  const int n16 = D.H / 8;
+  const int64_t units = (int64_t)D.N * D.T * n16;
+  const v4u* __restrict__ rs = reinterpret_cast<const v4u*>(comb);
+  v4u* __restrict__ os = reinterpret_cast<v4u*>(out);
+  for (int64_t tile = blockIdx.x; tile * kCombThreads < units; tile += gridDim.x) {
+    const int64_t u0 = tile * kCombThreads;
+    if (u0 + threadIdx.x >= units) continue;
+    int t0, tok, c;
+    os_tile_pos(u0, n16, t0, tok, c);
+    st16(os + u0 + threadIdx.x, recv_unit(D, rs, send_pos, topk_w, tok, c));
+  }
 }
 
 __global__ __launch_bounds__(kCombThreads) void k_comb_pull_os(Dims D, Ws W, const uint16_t* __restrict__ y,
@@ -285,7 +317,7 @@ __global__ __launch_bounds__(kCombThreads) void k_comb_pull_os(Dims D, Ws W, con
                                                             const int* __restrict__ send_pos,
                                                             const float* __restrict__ topk_w,
                                                             uint16_t* __restrict__ out) {
-  combine_os<CombMode::kPull, 2, kCombThreads>(D, W, y, idx, send_pos, topk_w, out);
+  combine_os<CombMode::kPull, kPullUnits, kCombThreads>(D, W, y, idx, send_pos, topk_w, out);
 }
 
 __global__ __launch_bounds__(kCombThreads) void k_comb_recv_partial_os(Dims D, Ws W, const uint16_t* __restrict__ comb,
@@ -520,8 +552,8 @@ __global__ __launch_bounds__(kPsThreads) void k_comb_send_partial(Dims D, Ws W, 
 int launch_comb_send(const Dims& D, const Ws& W, const uint16_t* y, const int* row_src, uint16_t* comb, int cus,
                      hipStream_t st) {
   if (D.N * D.TK == 0) return MOE_OK;
-  const int rc = launch("k_comb_send_os", k_comb_send_os, dim3(os_grid((int64_t)D.rows * (D.H / 8))),
-                        dim3(kOsThreads), 0, st, D, W, y, row_src, comb);
+  const int rc = launch("k_comb_send_os", k_comb_send_os, dim3(os_grid((int64_t)D.rows * (D.H / 8), kSendThreads)),
+                        dim3(kSendThreads), 0, st, D, W, y, row_src, comb);
   if (rc != MOE_OK || D.R == 0) return rc;   // packed regions never overflow
   return launch("k_comb_zero_dropped", k_comb_zero_dropped, dim3(cus), dim3(1024), 0, st, D, W, comb);
 }
@@ -536,7 +568,7 @@ int launch_comb_recv(const Dims& D, const uint16_t* comb, const int* send_pos, c
 int launch_comb_pull(const Dims& D, const Ws& W, const uint16_t* y, const int* idx, const int* send_pos,
                      const float* w, uint16_t* out, int cus, hipStream_t st) {
   if (D.N * D.T == 0) return MOE_OK;
-  return launch("k_comb_pull_os", k_comb_pull_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), 2 * kCombThreads)),
+  return launch("k_comb_pull_os", k_comb_pull_os, dim3(os_grid((int64_t)D.N * D.T * (D.H / 8), kPullUnits * kCombThreads)),
                 dim3(kCombThreads), 0, st, D, W, y, idx, send_pos, w, out);
 }
 
