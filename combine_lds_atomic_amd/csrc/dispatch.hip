@@ -125,11 +125,14 @@ __device__ __forceinline__ void pack_scales(const Dims& D, int h0, int h1, int r
 
 // Work item = (token, slice): slice sl of a token covers columns [h0, h1),
 // passes [sl*pps, (sl+1)*pps) of 1024 elements, pps = ceil(passes / slices).
-__device__ __forceinline__ void item_cols(const Dims& D, int item, int& tok, int& sl, int& h0, int& h1) {
+// Item i of a token is slice (i + rot) % slices: rotating the slices by the
+// round a packer wave is in (rot) hands each wave the short last slice in
+// turn rather than always or never.
+__device__ __forceinline__ void item_cols(const Dims& D, int item, int rot, int& tok, int& sl, int& h0, int& h1) {
   const int passes = (D.H + kPackCols - 1) / kPackCols;
   const int pps = (passes + D.slices - 1) / D.slices;
   tok = item / D.slices;
-  sl = item - tok * D.slices;
+  sl = (item - tok * D.slices + rot) % D.slices;
   h0 = sl * pps * kPackCols;
   h1 = min(D.H, (sl + 1) * pps * kPackCols);
 }
@@ -138,12 +141,12 @@ __device__ __forceinline__ void item_cols(const Dims& D, int item, int& tok, int
 // resolved (lane j < k: receive row of slot j, -1 for none).  LOADED: pa and
 // pb hold the item's first chunk.
 template <bool LOADED>
-__device__ __forceinline__ void pack_item(const Dims& D, int item, int row, const uint16_t* __restrict__ x,
+__device__ __forceinline__ void pack_item(const Dims& D, int item, int rot, int row, const uint16_t* __restrict__ x,
                                           uint8_t* __restrict__ recv_q, float* __restrict__ recv_s, float* ssw,
                                           const v4u* pa = nullptr, const v4u* pb = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   int tok, sl, h0, h1;
-  item_cols(D, item, tok, sl, h0, h1);
+  item_cols(D, item, rot, tok, sl, h0, h1);
   const uint16_t* xr = x + (int64_t)tok * D.H;
   int c0 = h0;
   if (LOADED) {   // the first chunk, peeled so its registers die here
@@ -542,10 +545,15 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     // Packers: work items (token, slice) interleaved over the workgroups
     // (wave w of packer p takes items 4p + w, then every 4*npack-th), so
     // the packers resident at any moment cover a compact band of tokens, as
-    // k_pack_os's grid does.
+    // k_pack_os's grid does.  Round r of the waves (items [r*stride,
+    // (r+1)*stride)) rotates the slices of its tokens by r when whole
+    // tokens make up a round, so that a wave's items are not all long or
+    // all short slices when the slices are unequal (7 passes in slices of
+    // 4 and 3 at H = 7168).
     const int p = wg - 2 * D.N - 1;
     const int items = D.N * D.T * D.slices;
     const int stride = npack * kLlWaves;
+    const int rstride = stride % D.slices == 0 ? stride : items;   // items per rotation step
     bool fail = false;
     // The workgroup's wait for the layout: one column's word (p % N: the
     // columns finish together, and the values a packer reads are each
@@ -637,16 +645,17 @@ __device__ __forceinline__ void dispatch_ll(const Dims& D, const Ws& W, const ui
     int e1 = -1;
     if (has) {
       int tok, sl, h0, h1;
-      item_cols(D, item, tok, sl, h0, h1);
+      item_cols(D, item, item / rstride, tok, sl, h0, h1);
       load_chunk(x + (int64_t)tok * D.H, h0, h1, lane, a, b);
       e1 = expert(item);
     }
     if (!DIRECT || x != nullptr) gate();
     if (has) {
-      pack_item<true>(D, item, resolve(item, e1), x, recv_q, recv_s, ssw, a, b);
+      pack_item<true>(D, item, item / rstride, resolve(item, e1), x, recv_q, recv_s, ssw, a, b);
       item += stride;
     }
-    for (; item < items; item += stride) pack_item<false>(D, item, resolve(item, expert(item)), x, recv_q, recv_s, ssw);
+    for (; item < items; item += stride)
+      pack_item<false>(D, item, item / rstride, resolve(item, expert(item)), x, recv_q, recv_s, ssw);
   }
   // The last workgroup of each group to finish clears the group's counter and
   // counts the group as done; the last group to finish advances every
