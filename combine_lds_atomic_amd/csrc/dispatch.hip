@@ -696,10 +696,14 @@ __global__ __launch_bounds__(kThreads) void k_dispatch_ll_direct(Dims D, Ws W, c
 // that map an expert-major row to its segment then read no global memory.
 constexpr int kStageInts = 2 * kMaxE + (kMaxE + kMaxN) + (kMaxE + 1) + (kMaxN + 1);
 
-// One region's routing tables staged in LDS, for the row searches.
+// One region's routing tables staged in LDS, for the row searches.  The
+// pointers carry the LDS address space: as plain pointers, merged with the
+// global ones of the other branch of unpack_row, they made every staged
+// read a flat access (and put a pointer through scratch).
+using lds_int = __attribute__((address_space(3))) int;
 struct UnpackStage {
-  int d0;                      // the region (-1: none staged)
-  int *sie, *so, *eo, *ro;     // src_in_exp / send_off columns, exp_off, recv_off of region d0
+  int d0;                                // the region (-1: none staged)
+  lds_int *sie, *so, *eo, *ro;           // src_in_exp / send_off columns, exp_off, recv_off of region d0
 };
 
 // Region d0 of the workgroup's first row lo (normally its only one):
@@ -712,7 +716,7 @@ __device__ __forceinline__ UnpackStage unpack_stage(const Dims& D, const Ws& W, 
                                                     int hi) {
   const int N = D.N, E = D.E, L = D.L;
   UnpackStage S;
-  S.sie = stage;
+  S.sie = (lds_int*)stage;
   S.so = S.sie + (N + 1) * L;
   S.eo = S.so + N * (L + 1);
   S.ro = S.eo + (L + 1);

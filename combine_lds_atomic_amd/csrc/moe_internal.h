@@ -226,7 +226,8 @@ __device__ __forceinline__ void os_tile_pos(int64_t u0, int per, int& g0, int& g
 }
 
 // Largest i in [0, n) with a[i*stride] <= v, for non-decreasing a with a[0] <= v.
-__device__ __forceinline__ int floor_index(const int* a, int n, int v, int stride = 1) {
+template <class P>
+__device__ __forceinline__ int floor_index(P a, int n, int v, int stride = 1) {
   int lo = 0, hi = n;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
