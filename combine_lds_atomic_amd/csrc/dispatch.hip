@@ -776,8 +776,8 @@ __device__ __forceinline__ void unpack_row(const Dims& D, const Ws& W, const Unp
 
 // ------------------------------------------------------------------ one-shot unpack
 //
-// The receive half in the one-shot form (kOsThreads threads per workgroup,
-// one 16-byte unit per thread, workgroups in row order): first
+// The receive half in the one-shot form (one 16-byte unit per thread,
+// workgroups in row order; 64 or 256 threads each, see launch_unpack): first
 // k_unpack_index maps every valid expert-major row g (region order) to the
 // source-major row it copies -- the segment search of unpack_row, with the
 // workgroup's region tables staged in LDS -- writing row_src and the pair
