@@ -40,7 +40,6 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxH = 32768;
 constexpr int kScaleBlock = 128;     // elements per fp32 scale
-constexpr int kMaxNB = kMaxH / kScaleBlock;
 // Routing chunk: slots of one rank handled by one workgroup of the count
 // kernel; every wave takes a contiguous quarter, 64 slots per batch.  The
 // chunk is 256..4096 slots, chosen per shape so that small batches still
