@@ -716,6 +716,29 @@ def summary(r):
     }
 
 
+def latency_model(points):
+    """Per phase, the fit t = alpha + bytes / beta over the workloads of one
+    run (points: phase -> [(algorithmic bytes, us)]), least squares on the
+    relative residuals so that the small workloads fix alpha (the fixed cost
+    per call: launches, routing latency) and the large ones beta (the
+    streaming rate).  Phases with fewer than three workloads are left out."""
+    import numpy as np
+    out = {}
+    for phase, pts in points.items():
+        if len(pts) < 3:
+            continue
+        b = np.array([p[0] for p in pts], dtype=np.float64) / 1e9   # GB
+        t = np.array([p[1] for p in pts], dtype=np.float64)         # us
+        A = np.stack([np.ones_like(b), b], axis=1) / t[:, None]
+        (alpha, slope), *_ = np.linalg.lstsq(A, np.ones_like(t), rcond=None)
+        fit = alpha + slope * b
+        out[phase] = {"alpha_us": round(float(alpha), 2),
+                      "beta_GB/s": round(float(1e6 / slope), 1) if slope > 0 else None,
+                      "workloads": len(pts),
+                      "max_rel_residual": round(float(np.max(np.abs(fit - t) / t)), 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -724,6 +747,9 @@ def main():
     ap.add_argument("--workload", default="combine_heavy", help="the headline workload")
     ap.add_argument("--workloads", default="all",
                     help="other workloads measured in the same run: all, none, or a comma-separated list")
+    ap.add_argument("--shape", default=None,
+                    help="N,T,H,E,k: time a uniformly routed workload of this shape as the headline instead")
+    ap.add_argument("--seed", type=int, default=None, help="input seed of the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     args = ap.parse_args()
@@ -738,6 +764,15 @@ def main():
     import workloads as W
 
     cfg = W.CONFIGS[args.workload]
+    if args.shape:
+        try:
+            N, T, H, E, k = (int(v) for v in args.shape.split(","))
+        except ValueError:
+            raise SystemExit("--shape takes N,T,H,E,k")
+        cfg = W.Config("custom", N=N, T=T, H=H, E=E, k=k, seed=0x7A11_00FF,
+                       note=f"T={T}, H={H}, E={E}, k={k}, N={N}, uniform routing")
+    if args.seed is not None:
+        cfg = cfg.with_(seed=args.seed)
     others = [] if args.workloads == "none" else (
         [w for w in ALL_WORKLOADS if w != cfg.name] if args.workloads == "all" else
         [w for w in args.workloads.split(",") if w and w != cfg.name])
@@ -762,10 +797,13 @@ def main():
     note(f"gpu: {cfg.name}, {args.warmup} warm-up and {args.steps} timed steps")
     res, total, step_ms = measure(cfg, args, dev, stream, hip, sweep=True)
     wl = {}
+    points = {p: [(d["alg_bytes"], d["us"])] for p, d in res["phases"].items()}
     for name in others:
         note(f"gpu: {name}, {args.warmup} warm-up and {args.steps} timed steps")
         r, _, _ = measure(W.CONFIGS[name], args, dev, stream, hip)
         wl[name] = summary(r)
+        for p, d in r["phases"].items():
+            points[p].append((d["alg_bytes"], d["us"]))
 
     value = total / (step_ms * 1e-3) / 1e9
     line = {
@@ -785,6 +823,7 @@ def main():
     }
     line.update(res)
     line["workloads"] = wl
+    line["latency_model"] = latency_model(points)
     line["cpu_baseline"] = cpu_single
     line["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(line), flush=True)

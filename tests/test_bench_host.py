@@ -74,3 +74,26 @@ def test_read_and_written_bytes_add_up_to_the_phase_bytes(N, T, H, E, k, Tc):
     assert rw["combine_send"][0] == rw["combine_send"][1]
     assert rw["combine_recv"][1] == N * Tcc * H * 2                  # one bf16 row per token out
     assert rw["dispatch_send"][1] > (k / 2) * rw["dispatch_send"][0] * 0.97   # the pack writes about k/2 times what it reads
+
+
+def test_latency_model_recovers_alpha_and_beta():
+    """Points on an exact line t = alpha + bytes / beta give back alpha and
+    beta; a phase timed on fewer than three workloads gets no fit."""
+    alpha, beta = 12.5, 6300.0   # us, GB/s
+    sizes = [0.04e9, 0.3e9, 4.8e9, 15.0e9, 30.1e9]
+    pts = {"combine_send": [(b, alpha + b / 1e9 / beta * 1e6) for b in sizes],
+           "dispatch_send": [(1e9, 200.0), (2e9, 360.0)]}
+    fit = bench.latency_model(pts)
+    assert set(fit) == {"combine_send"}
+    f = fit["combine_send"]
+    assert abs(f["alpha_us"] - alpha) < 0.01 and abs(f["beta_GB/s"] - beta) < 0.1
+    assert f["workloads"] == len(sizes) and f["max_rel_residual"] < 1e-9
+
+
+def test_latency_model_weights_relative_error():
+    """A fixed cost that only the small points show is kept: the fit on
+    relative residuals does not let the large points swamp alpha."""
+    pts = {"p": [(0.05e9, 20.0), (0.1e9, 28.0), (5e9, 808.0), (10e9, 1600.0)]}
+    f = bench.latency_model(pts)["p"]
+    assert 10.0 < f["alpha_us"] < 15.0
+    assert 6000.0 < f["beta_GB/s"] < 6400.0
