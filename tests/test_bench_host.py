@@ -2,7 +2,7 @@
 behind every GB/s figure (each phase's inputs read once and outputs written
 once, counted here from the arrays the calls take), the (token, destination
 rank) group count of the send-side partial combine (brute force), and the
-one-GPU guard of --gpus."""
+one-GPU guard of --gpus, the latency fit and the --shape check."""
 import subprocess
 import sys
 
@@ -97,3 +97,12 @@ def test_latency_model_weights_relative_error():
     f = bench.latency_model(pts)["p"]
     assert 10.0 < f["alpha_us"] < 15.0
     assert 6000.0 < f["beta_GB/s"] < 6400.0
+
+
+def test_malformed_shape_is_rejected_before_any_gpu_work():
+    """--shape takes five integers; anything else ends the run with a
+    message before a device is touched."""
+    r = subprocess.run([sys.executable, "bench.py", "--shape", "16,128,7168", "--no-cpu-baseline"],
+                       capture_output=True, text=True, cwd=bench.ROOT, timeout=300)
+    assert r.returncode != 0
+    assert "N,T,H,E,k" in (r.stdout + r.stderr)
