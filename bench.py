@@ -108,6 +108,15 @@ def _kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
+def _build_info():
+    """The commit the libraries were built from (written by build.py), if known."""
+    p = os.path.join(ROOT, "combine_lds_atomic_amd", "build_info.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        return json.load(fh)
+
+
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -820,6 +829,7 @@ def main():
         "dtype": DTYPE,
         "data": "synthetic",
         "sources_digest": _kernel_sources_digest(),
+        "build": _build_info(),
     }
     line.update(res)
     line["workloads"] = wl

@@ -10,6 +10,8 @@ declared symbol.
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -41,12 +43,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmoe_ep")
 
 
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
 def build(verbose: bool = False, out: str = LIB, extra_flags: list[str] | None = None) -> str:
-    """Build libmoe_ep.so at `out` and, beside the default one, libmoe_streams.so."""
+    """Build libmoe_ep.so at `out` and, beside the default one, libmoe_streams.so
+    and build_info.json (the commit and the kernel sources the libraries were
+    built from, for the benchmark's record)."""
     lib = _build_lib(SOURCES, out, "obj", verbose, extra_flags)
     if out == LIB:
         _build_lib(STREAMS_SOURCES, STREAMS_LIB, "obj_streams", verbose, extra_flags)
+        _write_build_info()
     return lib
+
+
+def sources_digest() -> str:
+    """First 16 hex digits of the SHA-256 of the kernel sources (csrc/, in name order)."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _write_build_info() -> None:
+    def git(*args):
+        r = subprocess.run(["git", *args], cwd=ROOT, capture_output=True, text=True)
+        return r.stdout.strip() if r.returncode == 0 else None
+    sha = git("rev-parse", "HEAD")
+    status = git("status", "--porcelain", "--", "combine_lds_atomic_amd/csrc", "include")
+    info = {"git_sha": sha, "kernel_sources_modified": bool(status) if status is not None else None,
+            "sources_digest": sources_digest()}
+    with open(BUILD_INFO, "w") as fh:
+        json.dump(info, fh)
 
 
 def _build_lib(sources: list[str], out: str, objsub: str, verbose: bool, extra_flags: list[str] | None) -> str:
