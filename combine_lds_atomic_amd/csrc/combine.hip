@@ -166,7 +166,8 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
   constexpr int kTile = TH * U;
   constexpr int kOsSlotTable = os_tile_tokens<U, TH>() * kMaxK;
   __shared__ int t_row[kOsSlotTable];
-  __shared__ float t_w[kOsSlotTable];
+  // (group rows carry weight 1: the partial receive keeps no weights)
+  __shared__ float t_w[MODE == CombMode::kRecvPartial ? 1 : kOsSlotTable];
   __shared__ int t_dest[MODE == CombMode::kRecvPartial ? kOsSlotTable : 1];
   const int n16 = D.H / 8, k = D.k;
   const int64_t units = (int64_t)D.N * D.T * n16;
@@ -195,31 +196,19 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
         row = em_row_of(D, W, s, e, sp);
       }
       t_row[i] = row;
-      if constexpr (MODE == CombMode::kRecvPartial) t_w[i] = 1.0f;
-      else t_w[i] = topk_w[slot];
+      if constexpr (MODE != CombMode::kRecvPartial) t_w[i] = topk_w[slot];
     }
     if constexpr (MODE == CombMode::kRecvPartial) {
       // A slot with a row leads its group unless an earlier slot of the
       // token has a row on the same rank; only leaders' group rows are summed.
+      // The test reads t_dest only, so each entry drops its own row in one
+      // pass.
       __syncthreads();
-      constexpr int kQ = kOsSlotTable / TH + 1;
-      bool lead[kQ];
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const int i = threadIdx.x + q * TH;
-        lead[q] = false;
-        if (i < nt * k) {
-          const int j = i % k, b = i - j, d = t_dest[i];
-          bool l = d >= 0;
-          for (int jj = 0; jj < j; ++jj) l = l && t_dest[b + jj] != d;
-          lead[q] = l;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const int i = threadIdx.x + q * TH;
-        if (i < nt * k && !lead[q]) t_row[i] = -1;
+      for (int i = threadIdx.x; i < nt * k; i += TH) {
+        const int j = i % k, b = i - j, d = t_dest[i];
+        bool l = d >= 0;
+        for (int jj = 0; jj < j; ++jj) l = l && t_dest[b + jj] != d;
+        if (!l) t_row[i] = -1;
       }
     }
     __syncthreads();
@@ -234,7 +223,7 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
       }
       if (uu >= units) break;
       const int* tr = t_row + (tok - t0) * k;
-      const float* tw = t_w + (tok - t0) * k;
+      const float* tw = MODE == CombMode::kRecvPartial ? t_w : t_w + (tok - t0) * k;
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -248,7 +237,7 @@ __device__ __forceinline__ void combine_os(const Dims& D, const Ws& W, const uin
         }
 #pragma unroll
         for (int jj = 0; jj < kSlotGroup; ++jj)
-          if (rr[jj] >= 0) acc_row8(acc, tw[j0 + jj], v[jj]);
+          if (rr[jj] >= 0) acc_row8(acc, MODE == CombMode::kRecvPartial ? 1.0f : tw[j0 + jj], v[jj]);
       }
       st16(os + uu, pack_bf16x8(acc));
     }
